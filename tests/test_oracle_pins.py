@@ -1,0 +1,442 @@
+"""Pins of the CPU oracle against what the number formats, the mathematics and
+library routines fix, independent of the oracle's own code.
+
+Each `check_*` function takes no arguments, runs against whatever oracle build is
+currently bound (see `oracle.using`), and raises AssertionError on a mismatch.
+The pytest tests run them on the real oracle; `test_planted_mistakes_are_caught`
+runs them on copies of the oracle with a mistake planted in the C source and
+requires every such copy to fail at least one of them.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bruteforce import (bf16_bits_to_float, bf16_bits_to_fraction, bf16_nearest, e4m3_step,
+                        e4m3fn_decode, e4m3fn_decode_array, e4m3fn_nearest, exact_out_row)
+from gen import CONFIGS, make_inputs
+from golden_io import read_value_code_table, read_worked_example
+
+EPS = 1e-6
+
+
+def f2b(x) -> np.ndarray:
+    """float array -> bf16 bits via torch's cast (inputs for tests only)."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def ulp_dist_bf16(a, b) -> np.ndarray:
+    """Distance in bf16 steps between two bf16 bit arrays (ordered-integer mapping)."""
+    def ordered(x):
+        x = np.asarray(x, dtype=np.int32)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + (x & 0x7FFF))
+    return np.abs(ordered(a) - ordered(b))
+
+
+# ============================================================================ encoders
+def check_bf16_encoder_vs_torch_cast():
+    """binary32 -> bf16 must equal torch's float32 -> bfloat16 cast (RNE) on every class
+    of binary32: random bit patterns, subnormals, near-overflow, specials."""
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 2 ** 32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    extra = np.array([0, 0x80000000, 0x00000001, 0x007FFFFF, 0x00800000, 0x7F7FFFFF, 0x7F7F8000,
+                      0x7F7F7FFF, 0x3F808000, 0x3F818000, 0x3F80C000, 0x7F800000, 0xFF800000],
+                     dtype=np.uint32)
+    bits = np.concatenate([bits, extra, extra | 0x8000, np.arange(0x3F800000, 0x3F820000,
+                                                                  dtype=np.uint32)])
+    f = bits.view(np.float32)
+    fin = ~np.isnan(f)
+    ref = torch.from_numpy(f[fin].copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_from_double_array(f[fin].astype(np.float64))
+    bad = np.nonzero(ref != got)[0]
+    assert bad.size == 0, f"bf16 mismatch at {bits[fin][bad[:5]]}: torch {ref[bad[:5]]} oracle {got[bad[:5]]}"
+    with np.errstate(invalid="ignore"):
+        nan_out = oracle.bf16_from_double_array(f[~fin].astype(np.float64))
+    assert np.all(np.isnan(bf16_bits_to_float(nan_out)))
+
+
+def check_bf16_golden_rounding_points():
+    for value, code in read_value_code_table("bf16_rounding.txt"):
+        got = oracle.bf16_from_double(value)
+        assert got == code, f"bf16({value!r}) = {got:04X}, expected {code:04X}"
+
+
+def check_bf16_encoder_exact_on_doubles():
+    """binary64 inputs (one rounding) against exact-rational rounding, incl. near-ties."""
+    rng = np.random.default_rng(2)
+    base = f2b(rng.standard_normal(2000).astype(np.float32) * 10.0)
+    mid = [bf16_bits_to_fraction(b) * (1 + Fraction(1, 256)) for b in base if (b & 0x7F80) != 0x7F80]
+    xs = []
+    for m in mid[:600]:
+        for d in (Fraction(0), Fraction(1, 2 ** 45), -Fraction(1, 2 ** 45)):
+            xs.append(float(m * (1 + d)))
+    xs += list(rng.standard_normal(2000) * 3.0)
+    got = oracle.bf16_from_double_array(np.array(xs))
+    for x, g in zip(xs, got):
+        want = bf16_nearest(Fraction(x), negative_zero=(x == 0 and np.signbit(x)))
+        assert g == want, f"bf16({x!r}) = {g:04X}, exact {want:04X}"
+
+
+def check_e4m3_encoder_exhaustive_bf16():
+    """Every bf16 value -> E4M3: nearest code by search over all finite codes (ties to the
+    even code, |v| > 448 saturates), and torch's float8_e4m3fn cast where |v| <= 464."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        f = bf16_bits_to_float(bits).astype(np.float64)
+    got = oracle.e4m3fn_from_double_array(f)
+    fin = np.isfinite(f)
+    assert np.all((got[np.isnan(f)] & 0x7F) == 0x7F)
+    assert np.all(got[np.isinf(f)] == np.where(f[np.isinf(f)] > 0, 0x7E, 0xFE))
+    # search over the code table, vectorised: distances to all 127 non-negative finite codes
+    vals = np.array([float(v) for _, v in __import__("bruteforce").E4M3_POS])
+    a = np.minimum(np.abs(f[fin]), 448.0)  # satfinite: beyond the largest code, the largest code
+    d = np.abs(a[:, None] - vals[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    even = cand & (np.arange(127)[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    want = pick.astype(np.uint8) | np.where(np.signbit(f[fin]), 0x80, 0).astype(np.uint8)
+    bad = np.nonzero(got[fin] != want)[0]
+    assert bad.size == 0, f"e4m3 mismatch at {f[fin][bad[:5]]}: {got[fin][bad[:5]]} vs {want[bad[:5]]}"
+    small = fin & (np.abs(f) <= 464)
+    ref = torch.from_numpy(f[small].astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ref, got[small])
+
+
+def check_e4m3_encoder_exact_near_ties():
+    """binary64 values just above / below each E4M3 midpoint round away from the tie."""
+    vals = [v for _, v in __import__("bruteforce").E4M3_POS]
+    xs = []
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        m = (lo + hi) / 2
+        for d in (Fraction(0), Fraction(1, 2 ** 40), -Fraction(1, 2 ** 40)):
+            xs.append(float(m * (1 + d)))
+    got = oracle.e4m3fn_from_double_array(np.array(xs))
+    for x, g in zip(xs, got):
+        assert g == e4m3fn_nearest(Fraction(x)), f"e4m3({x!r}) = {g:02X}"
+
+
+def check_e4m3_golden_codes():
+    for value, code in read_value_code_table("e4m3fn_codes.txt"):
+        got = oracle.e4m3fn_from_double(value)
+        assert got == code, f"e4m3({value!r}) = {got:02X}, expected {code:02X}"
+        if code not in (0x7F, 0xFF) and abs(value) <= 448 and e4m3fn_decode(code) == Fraction(value):
+            assert float(e4m3fn_decode(code)) == value
+
+
+# ============================================================================ worked examples
+def check_worked_example_plain():
+    g = read_worked_example("worked_example_plain.txt")
+    ro, out = oracle.reduce_add_rmsnorm(g["partials"], g["residual"], g["gamma"], EPS)
+    assert np.array_equal(ro, g["residual_out"]), (ro, g["residual_out"])
+    assert np.array_equal(out, g["out"]), ([hex(x) for x in out.ravel()], g["out"])
+
+
+def check_worked_example_quant():
+    g = read_worked_example("worked_example_quant.txt")
+    ro, out, q, sc = oracle.reduce_add_rmsnorm_quant_group(g["partials"], None, g["gamma"], EPS, 128)
+    assert np.array_equal(ro, g["residual_out"])
+    assert np.array_equal(out, g["out"])
+    assert np.array_equal(q, g["q"]), q
+    num, den = g["scale"].split("/")
+    assert sc[0, 0] == np.float32(float(num)) / np.float32(float(den))
+
+
+# ============================================================================ steps 1-3
+def check_integer_sums_exact():
+    """Small-integer partials and residual are exact in bf16 and their sums exact in fp32 in
+    any order, so residual_out is the integer sum, for every R."""
+    rng = np.random.default_rng(3)
+    for R in range(1, 9):
+        P = rng.integers(-16, 17, size=(R, 5, 16))
+        res = rng.integers(-16, 17, size=(5, 16))
+        g = f2b(np.ones(16))
+        ro, _ = oracle.reduce_add_rmsnorm(f2b(P), f2b(res), g, EPS)
+        want = P.sum(axis=0) + res
+        assert np.array_equal(bf16_bits_to_float(ro), want.astype(np.float32)), R
+
+
+def check_fold_order_and_precision():
+    """Hand-built rows whose bf16 result depends on the order and precision of the sum.
+    P = [1, 2^-8, 2^-24, 2^-24]: a binary32 left fold absorbs each 2^-24 (a tie at 1 + 2^-8,
+    kept by ties-to-even), leaving 1 + 2^-8, a bf16 tie that rounds to 1.0 (0x3F80); a reversed
+    fold or a binary64 sum keeps 2^-23 and rounds up to 0x3F81.
+    P = [2^-24, 1, 2^-8] with residual 2^-24: residual added last gives 0x3F80; the residual
+    added first keeps 2^-23 and gives 0x3F81."""
+    g = f2b(np.ones(8))
+    P = f2b(np.array([1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24])[:, None, None] * np.ones((1, 1, 8)))
+    ro, _ = oracle.reduce_add_rmsnorm(P, None, g, EPS)
+    assert np.all(ro == 0x3F80), ro
+    P = f2b(np.array([2.0 ** -24, 1.0, 2.0 ** -8])[:, None, None] * np.ones((1, 1, 8)))
+    ro, _ = oracle.reduce_add_rmsnorm(P, f2b(np.full((1, 8), 2.0 ** -24)), g, EPS)
+    assert np.all(ro == 0x3F80), ro
+
+
+def check_identities():
+    """R=1 without residual returns P_0 bit for bit; P_1 = -P_0 returns the residual;
+    negating every input negates residual_out and out exactly (RNE is symmetric)."""
+    d = make_inputs(CONFIGS["tiny"], seed=11, R=1, T=5, H=64)
+    ro, _ = oracle.reduce_add_rmsnorm(d["partials"], None, d["gamma"], EPS)
+    assert np.array_equal(ro, d["partials"][0])
+    d = make_inputs(CONFIGS["tiny"], seed=12, R=2, T=5, H=64)
+    P = d["partials"].copy()
+    P[1] = P[0] ^ 0x8000
+    ro, _ = oracle.reduce_add_rmsnorm(P, d["residual"], d["gamma"], EPS)
+    assert np.array_equal(bf16_bits_to_float(ro), bf16_bits_to_float(d["residual"]))
+    d = make_inputs(CONFIGS["tiny"], seed=13, R=5, T=6, H=256)
+    ro1, o1, q1, s1 = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS)
+    ro2, o2, q2, s2 = oracle.reduce_add_rmsnorm_quant_group(d["partials"] ^ 0x8000, d["residual"] ^ 0x8000,
+                                                           d["gamma"], EPS)
+    nz = (ro1 & 0x7FFF) != 0
+    assert np.array_equal(ro1[nz] ^ 0x8000, ro2[nz])
+    nz = (o1 & 0x7FFF) != 0
+    assert np.array_equal(o1[nz] ^ 0x8000, o2[nz])
+    assert np.array_equal(s1, s2)
+    nz = (q1 & 0x7F) != 0
+    assert np.array_equal(q1[nz] ^ 0x80, q2[nz])
+
+
+def check_reduce_vs_exact_sum():
+    """residual_out against the bf16 nearest to the exact rational sum: equal except where the
+    fp32 fold moved a value across a bf16 rounding boundary, and never more than 1 step off."""
+    n_eq = n_all = 0
+    for R, T, H, seed in [(2, 4, 256, 0), (1, 5, 16, 1), (3, 5, 16, 2), (8, 5, 16, 3), (6, 3, 64, 4)]:
+        d = make_inputs(CONFIGS["tiny"], seed=seed, R=R, T=T, H=H)
+        ro, _ = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS)
+        for t in range(T):
+            for h in range(H):
+                s = sum(bf16_bits_to_fraction(d["partials"][r, t, h]) for r in range(R))
+                s += bf16_bits_to_fraction(d["residual"][t, h])
+                want = bf16_nearest(s)
+                n_all += 1
+                n_eq += int(want == ro[t, h]) or int((want & 0x7FFF) == 0 and (ro[t, h] & 0x7FFF) == 0)
+                assert ulp_dist_bf16([want], [ro[t, h]])[0] <= 1, (R, t, h)
+    assert n_eq >= 0.99 * n_all, (n_eq, n_all)
+
+
+# ============================================================================ steps 4-5
+def check_norm_vs_exact():
+    """out for tiny shapes equals the bf16 nearest to y*rstd*gamma with rstd from the exact
+    mean of squares (60-digit decimal): the oracle's binary64 statistics must not move any
+    bf16 result on these inputs."""
+    for R, T, H, seed in [(2, 4, 256, 0), (1, 5, 16, 5), (4, 5, 16, 6), (8, 2, 48, 7)]:
+        d = make_inputs(CONFIGS["tiny"], seed=seed, R=R, T=T, H=H)
+        ro, out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS)
+        for t in range(T):
+            want = exact_out_row(list(ro[t]), list(d["gamma"]), EPS)
+            assert list(out[t]) == want, (R, T, H, t)
+
+
+def check_constant_rows():
+    """A constant row y = c gives out = bf16(c/sqrt(c^2 + eps) * gamma): eps is added to the mean
+    inside the square root. For |c| >> 1e-3 that is gamma * sign(c) bit for bit."""
+    H = 256
+    gamma = f2b(np.random.default_rng(4).uniform(0.5, 1.5, H))
+    for c in (1.0, -2.0, 0.5, 3.0, 2.0 ** -10, 2.0 ** -12, -(2.0 ** -9)):
+        P = f2b(np.full((1, 1, H), c))
+        ro, out = oracle.reduce_add_rmsnorm(P, None, gamma, EPS)
+        cf = Fraction(float(bf16_bits_to_float(P[0, 0, :1])[0]))
+        want = exact_out_row([P[0, 0, 0]] * H, list(gamma), EPS)
+        assert list(out[0]) == want, c
+        if abs(c) >= 0.5:
+            assert np.array_equal(out[0], gamma ^ (0x8000 if c < 0 else 0)), c
+        # the closed form, checked on the first element in float terms
+        exact = float(cf) / np.sqrt(float(cf) ** 2 + float(np.float32(EPS)))
+        exact *= float(bf16_bits_to_float(gamma[:1])[0])
+        assert abs(float(bf16_bits_to_float(out[0, :1])[0]) - exact) <= 2 ** -8 * abs(exact), c  # half a bf16 step
+
+
+def check_vs_torch_rms_norm():
+    """R = 1 without residual is plain RMSNorm: torch.nn.functional.rms_norm in float64 on the CPU,
+    rounded to bf16 by the exact-rational rounding (not through binary32)."""
+    for T, H, seed in [(4, 256, 0), (5, 16, 1), (8, 4096, 2), (3, 7168, 3)]:
+        d = make_inputs(CONFIGS["tiny"], seed=seed, R=1, T=T, H=H)
+        x = torch.from_numpy(bf16_bits_to_float(d["partials"][0]).astype(np.float64))
+        w = torch.from_numpy(bf16_bits_to_float(d["gamma"]).astype(np.float64))
+        ref = torch.nn.functional.rms_norm(x, (H,), weight=w, eps=float(np.float32(EPS))).numpy()
+        want = oracle.bf16_from_double_array(ref)  # pinned above to exact rounding
+        _, out = oracle.reduce_add_rmsnorm(d["partials"], None, d["gamma"], EPS)
+        dist = ulp_dist_bf16(out, want)
+        assert dist.max() <= 1 and (dist == 0).mean() >= 0.999, (T, H, dist.max(), (dist == 0).mean())
+
+
+def check_constant_gamma_rms():
+    """With gamma = c everywhere, RMS(out) = |c| * sqrt(ms / (ms + eps)) up to bf16 rounding."""
+    d = make_inputs(CONFIGS["tiny"], seed=21, R=3, T=6, H=1024)
+    for c in (1.0, 0.25, -3.0):
+        gamma = f2b(np.full(1024, c))
+        ro, out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], gamma, EPS)
+        y = bf16_bits_to_float(ro).astype(np.float64)
+        ms = (y ** 2).mean(axis=1)
+        rms = np.sqrt((bf16_bits_to_float(out).astype(np.float64) ** 2).mean(axis=1))
+        want = abs(c) * np.sqrt(ms / (ms + float(np.float32(EPS))))
+        assert np.all(np.abs(rms - want) <= 2 ** -8 * abs(c)), (c, rms, want)
+
+
+def check_scale_invariance():
+    """Scaling every partial and the residual by 4 (exact in bf16) scales residual_out by 4 exactly
+    and leaves out unchanged but for eps, which may move a rare element by one bf16 step."""
+    d = make_inputs(CONFIGS["tiny"], seed=22, R=4, T=8, H=512)
+    ro1, o1 = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS)
+    up = lambda b: np.where((b & 0x7F80) != 0, b + (2 << 7), b).astype(np.uint16)  # exponent + 2
+    ro2, o2 = oracle.reduce_add_rmsnorm(up(d["partials"]), up(d["residual"]), d["gamma"], EPS)
+    assert np.array_equal(bf16_bits_to_float(ro2), 4 * bf16_bits_to_float(ro1))
+    dist = ulp_dist_bf16(o1, o2)
+    assert dist.max() <= 1 and (dist == 0).mean() >= 0.999
+
+
+# ============================================================================ step 6
+def _quant_case(seed, R, T, H, outliers=True):
+    cfg = CONFIGS["decode_fp8"] if outliers else CONFIGS["tiny"]
+    d = make_inputs(cfg, seed=seed, R=R, T=T, H=H)
+    return d, oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS, 128)
+
+
+def check_quant_scale_and_max_code():
+    """scale = binary32(amax / 448) recomputed from the group's bf16 out with IEEE single division,
+    and every group with amax > 0 holds a code of magnitude 448 (0x7E)."""
+    for seed, R, T, H in [(0, 4, 16, 4096), (1, 2, 3, 256), (2, 8, 2, 1024)]:
+        d, (ro, out, q, sc) = _quant_case(seed, R, T, H)
+        o = np.abs(bf16_bits_to_float(out)).reshape(T, H // 128, 128)
+        amax = o.max(axis=2).astype(np.float32)
+        assert np.array_equal(sc, amax / np.float32(448.0))
+        qq = q.reshape(T, H // 128, 128) & 0x7F
+        assert np.all((qq == 0x7E).any(axis=2) | (amax == 0))
+
+
+def check_quant_codes_exact_small():
+    """Codes equal the nearest E4M3 (by search) to the exact quotient out/scale, on tiny shapes."""
+    for seed, R, T, H in [(3, 2, 2, 128), (4, 4, 1, 256)]:
+        d, (ro, out, q, sc) = _quant_case(seed, R, T, H)
+        for t in range(T):
+            for h in range(H):
+                s = sc[t, h // 128]
+                v = bf16_bits_to_fraction(out[t, h]) / Fraction(float(s))
+                want = e4m3fn_nearest(v, negative_zero=(out[t, h] == 0x8000))
+                assert q[t, h] == want, (t, h, q[t, h], want)
+
+
+def check_quant_dequant_bound():
+    """|decode(q) * scale - out| <= (step(v)/2 + 2^-20 |v|) * scale with v = out/scale."""
+    for seed, R, T, H in [(5, 4, 16, 4096), (6, 8, 4, 7168)]:
+        d, (ro, out, q, sc) = _quant_case(seed, R, T, H)
+        o = bf16_bits_to_float(out).astype(np.float64)
+        s = np.repeat(sc.astype(np.float64), 128, axis=1)
+        deq = e4m3fn_decode_array(q) * s
+        v = o / s
+        step = np.vectorize(e4m3_step)(v)
+        assert np.all(np.abs(deq - o) <= (step / 2 + 2.0 ** -20 * np.abs(v)) * s)
+
+
+def check_quant_zero_group_and_consistency():
+    """An all-zero group gives scale 0 and codes 0; the FP8 call's residual_out / out equal the
+    plain call's; emitting out or not changes nothing else."""
+    d = make_inputs(CONFIGS["tiny"], seed=31, R=2, T=3, H=384)
+    P = d["partials"].copy()
+    res = d["residual"].copy()
+    P[1, 1, 128:256] = P[0, 1, 128:256] ^ 0x8000  # cancels exactly
+    res[1, 128:256] = 0
+    ro, out, q, sc = oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], EPS)
+    assert sc[1, 1] == 0 and np.all(q[1, 128:256] == 0)
+    assert np.all(sc[[0, 2]] > 0)
+    ro2, out2 = oracle.reduce_add_rmsnorm(P, res, d["gamma"], EPS)
+    assert np.array_equal(ro, ro2) and np.array_equal(out, out2)
+    ro3, none, q3, sc3 = oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], EPS, emit_out=False)
+    assert none is None and np.array_equal(ro, ro3) and np.array_equal(q, q3) and np.array_equal(sc, sc3)
+
+
+def check_in_place_residual():
+    d = make_inputs(CONFIGS["tiny"], seed=41, R=3, T=4, H=256)
+    ro, out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS)
+    ro2, out2 = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS, in_place=True)
+    assert np.array_equal(ro, ro2) and np.array_equal(out, out2)
+
+
+ALL_CHECKS = [
+    check_bf16_encoder_vs_torch_cast, check_bf16_golden_rounding_points, check_bf16_encoder_exact_on_doubles,
+    check_e4m3_encoder_exhaustive_bf16, check_e4m3_encoder_exact_near_ties, check_e4m3_golden_codes,
+    check_worked_example_plain, check_worked_example_quant,
+    check_integer_sums_exact, check_fold_order_and_precision, check_identities, check_reduce_vs_exact_sum,
+    check_norm_vs_exact, check_constant_rows, check_vs_torch_rms_norm, check_constant_gamma_rms,
+    check_scale_invariance,
+    check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_dequant_bound,
+    check_quant_zero_group_and_consistency, check_in_place_residual,
+]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__[len("check_"):])
+def test_pin(check):
+    check()
+
+
+# ============================================================================ planted mistakes
+# Each entry: (name, text in farn_oracle.c, replacement[, text, replacement ...]).
+# Each mutant must fail at least one pin.
+MUTANTS = [
+    ("drop_residual", "y32 = acc + bf16_to_float(j->residual[base + h]);", "y32 = acc;"),
+    ("drop_rank_1", "for (int r = 1; r < j->R; ++r)", "for (int r = 2; r < j->R; ++r)"),
+    ("double_count_rank_0", "float acc = bf16_to_float(j->partials[0][base + h]);",
+     "float acc = 2.0f * bf16_to_float(j->partials[0][base + h]);"),
+    ("fold_reversed", "for (int r = 1; r < j->R; ++r) acc = acc + bf16_to_float(j->partials[r][base + h]);",
+     "acc = bf16_to_float(j->partials[j->R - 1][base + h]); "
+     "for (int r = j->R - 2; r >= 0; --r) acc = acc + bf16_to_float(j->partials[r][base + h]);"),
+    ("fold_in_double", "        float y32 = acc;\n        if (j->residual) y32 = acc + bf16_to_float(j->residual[base + h]);",
+     "        double dacc = 0; for (int r = 0; r < j->R; ++r) dacc += bf16_to_float(j->partials[r][base + h]);\n"
+     "        float y32 = (float)dacc;\n        if (j->residual) y32 = (float)(dacc + bf16_to_float(j->residual[base + h]));"),
+    ("residual_first", "        float acc = bf16_to_float(j->partials[0][base + h]);",
+     "        float acc = bf16_to_float(j->partials[0][base + h]);\n"
+     "        if (j->residual) acc = bf16_to_float(j->residual[base + h]) + acc;",
+     "if (j->residual) y32 = acc + bf16_to_float(j->residual[base + h]);", ""),
+    ("residual_wrong_row", "j->residual[base + h]", "j->residual[h]"),
+    ("mean_divisor", "ss / (double)H", "ss / (double)(H - 1)"),
+    ("eps_outside_sqrt", "1.0 / sqrt(ss / (double)H + (double)j->eps)",
+     "1.0 / (sqrt(ss / (double)H) + (double)j->eps)"),
+    ("eps_dropped", "1.0 / sqrt(ss / (double)H + (double)j->eps)", "1.0 / sqrt(ss / (double)H)"),
+    ("gamma_reversed", "bf16_to_double(j->gamma[h])", "bf16_to_double(j->gamma[H - 1 - h])"),
+    ("no_gamma", "y * rstd * bf16_to_double(j->gamma[h])", "y * rstd"),
+    ("scale_240", "amax / 448.0", "amax / 240.0"),
+    ("quant_truncates", "double r = nearbyint(a / quantum) * quantum; /* in [0, 448] */",
+     "double r = floor(a / quantum) * quantum;"),
+    ("bf16_truncates", "double r = nearbyint(a / quantum) * quantum;\n    if (r >= 0x1p128)",
+     "double r = trunc(a / quantum) * quantum;\n    if (r >= 0x1p128)"),
+    ("bf16_mantissa_6", "double quantum = ldexp(1.0, ex - 7);", "double quantum = ldexp(1.0, ex - 6);"),
+    ("e4m3_no_subnormals", "if (ex < -6) ex = -6;", "if (ex < -9) ex = -9;"),
+    ("group_offset", "const int64_t h0 = g * j->group;", "const int64_t h0 = g * j->group + (g > 0);"),
+    ("scale_transposed", "j->scales[t * G + g] = scale;", "j->scales[g * j->T + t] = scale;"),
+    ("abs_dropped", "double v = fabs(bf16_to_double(o[h]));", "double v = bf16_to_double(o[h]);"),
+    ("stats_on_gamma_scaled", "ss += y * y;", "ss += y * y * bf16_to_double(j->gamma[h]);"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistakes_are_caught(mutant, tmp_path):
+    name, edits = mutant[0], mutant[1:]
+    mutated = open(os.path.join(os.path.dirname(oracle.__file__), "farn_oracle.c")).read()
+    for old, new in zip(edits[0::2], edits[1::2]):
+        assert old in mutated, f"mutation anchor for {name} not found"
+        mutated = mutated.replace(old, new, 1)
+    c = tmp_path / "mut.c"
+    so = tmp_path / "mut.so"
+    c.write_text(mutated)
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
+    caught = []
+    with oracle.using(str(so)):
+        for check in ALL_CHECKS:
+            try:
+                check()
+            except AssertionError:
+                caught.append(check.__name__)
+            except Exception:  # a crash or bad status also counts as caught
+                caught.append(check.__name__ + "!")
+            if caught:
+                break
+    assert caught, f"planted mistake {name} passed every pin"
