@@ -1,0 +1,291 @@
+"""Bench of the fused reduce + residual-add + RMSNorm (+ FP8 group-128 quant) op on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant V]
+
+A step is one call of the FP8 entry point (reduce, residual add, bf16 round,
+RMSNorm, per-group E4M3 quant, size-based dispatch) over one batch already resident
+in HBM. The default workload is the prefill chunk R=8, T=8192, H=7168 with the bf16
+output emitted: 1,352,400,896 algorithmic bytes per call, well beyond the 256 MB
+Infinity Cache, so every call streams from HBM.
+
+Prints ONE JSON line: value = algorithmic bytes per step / time per step (GB/s), with
+the roofline of the kernel (HBM bound, 8 TB/s peak), the CPU oracle timed on host
+cores on the same workload, a parity gate against the oracle on sampled rows, and
+secondary figures for the decode shapes (us/call).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tp_all_reduce_amd as F  # noqa: E402  (raises if the HIP library is not built)
+from gen import CONFIGS, make_inputs, sweep_config  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
+METRIC = "effective HBM GB/s (% of MI355X peak) and µs/call of fused reduce+RMSNorm"
+KERNEL_SRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc", "farn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOADS = {
+    # name: (config, quant, emit_out)
+    "prefill_fp8": (CONFIGS["prefill"], True, True),
+    "prefill": (CONFIGS["prefill"], False, True),
+    "decode_ds": (CONFIGS["decode_ds"], False, True),
+    "decode_fp8": (CONFIGS["decode_fp8"], True, True),
+    "tiny": (CONFIGS["tiny"], False, True),
+}
+for _T in (2 ** k for k in range(1, 13)):
+    WORKLOADS[f"sweep_T{_T}"] = (sweep_config(_T), False, True)
+
+VARIANT_NAMES = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def describe(cfg, quant, emit_out):
+    q = ", FP8 group-128 quant" + (" + bf16 out" if emit_out else ", bf16 out not written") if quant else ""
+    return f"{cfg.what}: R={cfg.R} T={cfg.T} H={cfg.H}{q}"
+
+
+class Bufs:
+    """One set of device inputs and outputs for a workload."""
+
+    def __init__(self, d, dev, quant, emit_out):
+        from tests.parity import to_dev_bf16
+        self.R, self.T, self.H = d["R"], d["T"], d["H"]
+        self.P = [to_dev_bf16(d["partials"][r], dev) for r in range(self.R)]
+        self.res = to_dev_bf16(d["residual"], dev)
+        self.g = to_dev_bf16(d["gamma"], dev)
+        self.quant, self.emit_out = quant, emit_out
+        self.alloc_outputs(dev)
+
+    def alloc_outputs(self, dev):
+        T, H = self.T, self.H
+        self.ro = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if (self.emit_out or not self.quant) else None
+        self.q = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.quant else None
+        self.s = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.quant else None
+
+    def clone(self, dev):
+        c = object.__new__(Bufs)
+        c.R, c.T, c.H, c.quant, c.emit_out = self.R, self.T, self.H, self.quant, self.emit_out
+        c.P = [p.clone() for p in self.P]
+        c.res, c.g = self.res.clone(), self.g.clone()
+        c.alloc_outputs(dev)
+        return c
+
+    def call(self, variant, grid_cap=0):
+        if self.quant:
+            F.reduce_add_rmsnorm_quant_group(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
+                                             residual_out=self.ro, out=self.out, q=self.q, scales=self.s,
+                                             variant=variant, grid_cap=grid_cap)
+        else:
+            F.reduce_add_rmsnorm(self.P, self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
+                                 variant=variant, grid_cap=grid_cap)
+
+
+def nbytes(cfg, quant, emit_out):
+    return cfg.nbytes_quant(emit_out) if quant else cfg.nbytes_plain
+
+
+def time_calls(sets, variant, steps, warmup, grid_cap=0):
+    """Average ms per call over `steps` back-to-back calls, rotating over `sets`, timed with
+    events on the stream the kernels are launched on (torch's current stream)."""
+    for i in range(warmup):
+        sets[i % len(sets)].call(variant, grid_cap)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        sets[i % len(sets)].call(variant, grid_cap)
+    end.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return start.elapsed_time(end) / steps, wall / steps
+
+
+def parity_gate(d, bufs, quant, emit_out, rows):
+    import oracle
+    from tests.parity import compare_bf16, compare_fp8, from_dev_bf16, within_tolerance
+    P = d["partials"][:, rows, :]
+    res = d["residual"][rows]
+    if quant:
+        r_ro, r_out, r_q, r_s = oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], 1e-6, 128,
+                                                                      emit_out, nthreads=8)
+        fp8 = compare_fp8(bufs.q.cpu().numpy()[rows], r_q, bufs.s.cpu().numpy()[rows], r_s)
+    else:
+        r_ro, r_out = oracle.reduce_add_rmsnorm(P, res, d["gamma"], 1e-6, nthreads=8)
+        fp8 = None
+    rep_ro = compare_bf16("residual_out", from_dev_bf16(bufs.ro)[rows], r_ro)
+    rep_out = compare_bf16("out", from_dev_bf16(bufs.out)[rows], r_out) if bufs.out is not None else None
+    ok, why = within_tolerance(rep_ro, rep_out, fp8)
+    return {"ok": ok, "why": why, "rows_checked": int(len(rows)),
+            "residual_out_bit_diffs": rep_ro["n_bit_diff"],
+            "out_max_rel_err": None if rep_out is None else rep_out["max_rel_err"],
+            "out_bit_diffs": None if rep_out is None else rep_out["n_bit_diff"],
+            "fp8_code_diffs": None if fp8 is None else fp8["n_code_diff"],
+            "scale_max_rel_err": None if fp8 is None else fp8["max_scale_rel_err"]}
+
+
+def cpu_baseline(d, cfg, quant, emit_out, budget_s):
+    """The oracle as it stands, on the host cores, over whole passes of the workload until
+    about budget_s seconds have been spent."""
+    import oracle
+    threads = min(16, len(os.sched_getaffinity(0)))
+    passes, spent = 0, 0.0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        if quant:
+            oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], 1e-6, 128,
+                                                  emit_out, nthreads=threads)
+        else:
+            oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], 1e-6, nthreads=threads)
+        spent += time.perf_counter() - t0
+        passes += 1
+    gbps = nbytes(cfg, quant, emit_out) * passes / spent / 1e9
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} full pass(es) over the workload ({cfg.T} rows), {spent:.1f} s",
+            "ms_per_call": round(spent / passes * 1e3, 2)}
+
+
+def recorded_traffic(workload):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_hash():
+        return None  # counters were taken on another version of the kernel
+    return rec.get("bytes_per_launch")
+
+
+def secondary(dev, steps):
+    """Decode shapes (us/call, hot = one buffer set, cold = sets rotated over >= 1 GiB) and the
+    plain prefill call."""
+    out = {}
+    for name in ("decode_ds", "decode_fp8"):
+        cfg, quant, emit = WORKLOADS[name]
+        d = make_inputs(cfg)
+        b = Bufs(d, dev, quant, emit)
+        nb = nbytes(cfg, quant, emit)
+        hot, hot_wall = time_calls([b], F.VARIANT_AUTO, steps, 20)
+        k = max(1, -(-(1 << 30) // nb))
+        sets = [b] + [b.clone(dev) for _ in range(k - 1)]
+        cold, _ = time_calls(sets, F.VARIANT_AUTO, max(steps, 2 * k), 2 * k)
+        out[name] = {"us_per_call_hot": round(hot * 1e3, 2), "us_per_call_cold": round(cold * 1e3, 2),
+                     "us_per_call_wall_hot": round(hot_wall * 1e3, 2),
+                     "GBps_cold": round(nb / (cold * 1e-3) / 1e9, 1), "rotation_sets": k,
+                     "bytes_per_call": nb}
+        del sets, b
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--variant", default="auto", choices=sorted(VARIANT_NAMES))
+    ap.add_argument("--grid-cap", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one torch copy of 1 GiB (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    cfg, quant, emit_out = WORKLOADS[args.workload]
+    variant = VARIANT_NAMES[args.variant]
+
+    log(f"generating {args.workload}")
+    d = make_inputs(cfg)
+    bufs = Bufs(d, dev, quant, emit_out)
+    nb = nbytes(cfg, quant, emit_out)
+
+    parity = None
+    if not args.no_parity:
+        bufs.call(variant, args.grid_cap)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(1)
+        rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 32)]))
+        parity = parity_gate(d, bufs, quant, emit_out, rows)
+        log(f"parity: {parity}")
+        if not parity["ok"]:
+            print(json.dumps({"metric": METRIC, "error": "parity gate failed", "parity": parity}))
+            sys.exit(1)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+        del src, dst
+
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    ms, wall_ms = time_calls([bufs], variant, args.steps, args.warmup, args.grid_cap)
+    gbps = nb / (ms * 1e-3) / 1e9
+    ran = F.select_variant(cfg.R, cfg.T, cfg.H, quant) if variant == F.VARIANT_AUTO else variant
+    traffic = recorded_traffic(args.workload)
+    result = {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(cfg, quant, emit_out), "name": args.workload, "R": cfg.R,
+                   "T": cfg.T, "H": cfg.H, "quant": quant, "emit_bf16_out": emit_out,
+                   "variant": {1: "latency", 2: "bandwidth"}[ran], "bytes_per_step": nb,
+                   "seed": cfg.seed},
+        "us_per_call": round(ms * 1e3, 2), "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
+        "wall_us_per_call": round(wall_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
+                     "kernel": "farn_" + {1: "latency", 2: "bandwidth"}[ran],
+                     "algorithmic_bytes_per_launch": nb,
+                     "hbm_bytes_per_launch": traffic},
+        "parity": parity,
+    }
+    if args.cpu_budget > 0:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(d, cfg, quant, emit_out, args.cpu_budget)
+    if not args.no_secondary:
+        del bufs
+        torch.cuda.empty_cache()
+        log("secondary decode shapes")
+        result["secondary"] = secondary(dev, 200)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * farn.h - C ABI of the fused reduce + residual-add + RMSNorm (+ per-group FP8
+ * quant) op for AMD Instinct MI355X (gfx950).
+ *
+ * The op is the per-GPU body of a tensor-parallel all-reduce fused with the
+ * residual add and RMSNorm that follows it, with the R rank partial-sum buffers
+ * read from device memory. The pages' Python forms of the call are:
+ *   - fused_ar_rms(inp, res_inp, *, w, eps, registered, use_1stage) returning
+ *     (normalised output, all-reduce + residual output):
+ *     "ROCm AITER fused all-reduce + RMSNorm" (vLLM #37646 summary),
+ *     AiterCustomAllreduceProto and _rocm_aiter_fused_allreduce_rmsnorm_impl;
+ *   - tensor_model_parallel_fused_allreduce_rmsnorm_quant_per_group(x, residual,
+ *     weight, eps, group_size=128, emit_bf16) returning FP8 codes, per-group
+ *     scales, the residual output and optionally the bf16 output, or None when
+ *     the fused path cannot run: "AMD fused AllReduce-RMSNorm quant kernel"
+ *     (sglang #24651 summary), layernorm.py snippet.
+ * This ABI keeps their arguments, replaces the communicator with R explicit
+ * partial pointers and the returned tuples with named output pointers, and
+ * replaces "return None" with a status code.
+ *
+ * Arithmetic of one call, per token row t (h = 0..H-1):
+ *   acc   = P_0[t,h]; acc += P_r[t,h] for r = 1..R-1     fp32 adds, rank order
+ *   y     = acc + residual[t,h]                          fp32 (no add if residual == NULL)
+ *   residual_out[t,h] = bf16_rne(y)
+ *   rstd  = 1 / sqrt(sum_h residual_out[t,h]^2 / H + eps)   fp64, fixed reduction tree
+ *   out[t,h] = bf16_rne((residual_out[t,h] * rstd) * gamma[h])   fp64 product, one rounding
+ * and for the quant call, per group g of 128 channels:
+ *   scale[t,g] = amax_g |out| / 448  (fp32, correctly rounded)
+ *   q[t,h]     = e4m3fn_rne(out[t,h] / scale[t,g])  (OCP E4M3, satfinite; 0 when scale == 0;
+ *                one rounding of the exact quotient)
+ *
+ * Layout: every [T,H] buffer is row-major and contiguous (row stride H
+ * elements); bf16 values are passed as raw 16-bit patterns; q holds one E4M3
+ * byte per element; scales is fp32 [T, H/128] row-major.
+ *
+ * Ownership: the caller allocates and frees every buffer; the library never
+ * allocates, frees, synchronises, or keeps state between calls. Work is
+ * enqueued asynchronously on `stream` (a hipStream_t; NULL = default stream).
+ *
+ * Errors: every argument check runs on the host before anything is enqueued; a
+ * non-OK status means no work was enqueued (the analogue of the pages' "None,
+ * caller falls back"). T == 0 returns FARN_OK and enqueues nothing; the [T,H]
+ * buffers may then be NULL (gamma and the partials array may not).
+ * FARN_ERR_LAUNCH is returned when the launch itself fails.
+ */
+#ifndef FARN_H
+#define FARN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum farn_status {
+    FARN_OK = 0,
+    FARN_ERR_NULL = 1,    /* a required pointer is NULL */
+    FARN_ERR_SHAPE = 2,   /* R not in [1, FARN_MAX_R]; T < 0; H <= 0, H % 8 != 0 or
+                             H > FARN_MAX_H; quant: group_size != 128 or H % 128 != 0 */
+    FARN_ERR_ALIGN = 3,   /* a bf16 / q buffer is not 16-byte aligned, or scales not 4-byte aligned */
+    FARN_ERR_ALIAS = 4,   /* an output overlaps an input or another output (the one allowed
+                             overlap: residual_out == residual exactly, in place) */
+    FARN_ERR_EPS = 5,     /* eps is not finite or is negative */
+    FARN_ERR_LAUNCH = 6,  /* the kernel launch failed */
+    FARN_ERR_VARIANT = 7  /* unknown variant or negative grid cap in an _ex call */
+} farn_status;
+
+/* Largest TP degree the pages run is 8 ("[AMD] Support --enable-aiter-allreduce-fusion
+   on AMD GPUs", Commands Used: --tp 8). */
+#define FARN_MAX_R 8
+/* A row is held in registers: up to 1024 lanes x 4 vectors of 8 bf16. */
+#define FARN_MAX_H 32768
+/* Quant group along H ("per-1x128", group_size=128 in the sglang #24651 summary). */
+#define FARN_GROUP 128
+#define FARN_ABI_VERSION 1
+
+/*
+ * Plain call: reduce + residual add + RMSNorm.
+ *   partials      host array of R device pointers, each bf16 [T,H]; may alias each other
+ *   R             number of rank partials, 1..FARN_MAX_R
+ *   residual      device bf16 [T,H], or NULL for no residual
+ *   gamma         device bf16 [H]
+ *   eps           added to the mean of squares inside the square root (1e-6 typical)
+ *   T, H          tokens and hidden size
+ *   residual_out  device bf16 [T,H]; may equal residual (in place)
+ *   out           device bf16 [T,H]
+ *   stream        hipStream_t or NULL
+ */
+farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,
+                                    const void *gamma, float eps, int64_t T, int64_t H,
+                                    void *residual_out, void *out, void *stream);
+
+/*
+ * FP8 call: the plain call, then per-group E4M3 quant of the bf16 output.
+ *   group_size    must be FARN_GROUP (128); H % 128 == 0
+ *   residual_out  device bf16 [T,H]; may equal residual
+ *   out           device bf16 [T,H], or NULL to not write the bf16 output (emit_bf16 off)
+ *   q             device uint8 [T,H], E4M3 codes
+ *   scales        device fp32 [T, H/128]
+ */
+farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int R,
+                                                const void *residual, const void *gamma, float eps,
+                                                int64_t T, int64_t H, int group_size,
+                                                void *residual_out, void *out, void *q,
+                                                float *scales, void *stream);
+
+/* Kernel variants. AUTO picks by size (farn_select_variant). LATENCY: one workgroup
+   per token row. BANDWIDTH: persistent workgroups that stream many rows each. Both
+   compute bit-identical results. */
+typedef enum farn_variant {
+    FARN_VARIANT_AUTO = 0,
+    FARN_VARIANT_LATENCY = 1,
+    FARN_VARIANT_BANDWIDTH = 2
+} farn_variant;
+
+/* As the calls above, with the variant forced and, for BANDWIDTH, the number of
+   workgroups capped (grid_cap = 0: the library's choice). For tests and the bench. */
+farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
+                                       const void *gamma, float eps, int64_t T, int64_t H,
+                                       void *residual_out, void *out, void *stream,
+                                       int variant, int grid_cap);
+farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, int R,
+                                                   const void *residual, const void *gamma,
+                                                   float eps, int64_t T, int64_t H, int group_size,
+                                                   void *residual_out, void *out, void *q,
+                                                   float *scales, void *stream, int variant,
+                                                   int grid_cap);
+
+/* The variant AUTO would run for this shape (no validation; pure function of its arguments). */
+int farn_select_variant(int R, int64_t T, int64_t H, int quant);
+
+/* Static, NUL-terminated description of a status code. */
+const char *farn_status_string(int status);
+
+int farn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FARN_H */

@@ -1,0 +1,163 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every function
+include/farn.h declares, and rejects every malformed call with the documented status
+before touching the GPU. Pointers here are fake, aligned host addresses: the checks
+never dereference them, and every call below is rejected before any HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tp_all_reduce_amd as F
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "farn.h")
+L = F.lib()
+
+OK, NULL, SHAPE, ALIGN, ALIAS, EPS, LAUNCH, VARIANT = range(8)
+MiB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(farn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    declared = declared_functions()
+    assert set(declared) == set(F.EXPORTS), declared
+    nm = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r"\bT (farn_[a-z0-9_]+)$", nm, flags=re.M))
+    assert exported == set(declared), (exported, declared)
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (FARN_[A-Z_]+) (\d+)", text))
+    assert int(consts["FARN_MAX_R"]) == F.MAX_R
+    assert int(consts["FARN_MAX_H"]) == F.MAX_H
+    assert int(consts["FARN_GROUP"]) == F.GROUP
+    assert int(consts["FARN_ABI_VERSION"]) == F.abi_version()
+    names = re.findall(r"(FARN_(?:OK|ERR_[A-Z]+)) = (\d+)", text)
+    assert {int(v): k for k, v in names} == F.STATUS
+
+
+def test_status_strings_and_select():
+    for s in range(8):
+        assert L.farn_status_string(s)
+    assert L.farn_status_string(99) == b"unknown status"
+    for T in (1, 2, 64, 512):
+        assert F.select_variant(8, T, 7168, False) == F.VARIANT_LATENCY
+    for T in (4096, 8192, 1 << 20):
+        assert F.select_variant(8, T, 7168, True) == F.VARIANT_BANDWIDTH
+
+
+class FakeCall:
+    """A well-formed plain / FP8 call over fake, disjoint, 4 KiB-aligned host addresses."""
+
+    def __init__(self, R=2, T=4, H=256, quant=False):
+        self.R, self.T, self.H, self.quant = R, T, H, quant
+        base = 0x10_0000_0000
+        self.partials = [base + i * 16 * MiB for i in range(R)]
+        self.residual = base + 100 * 16 * MiB
+        self.gamma = base + 101 * 16 * MiB
+        self.residual_out = base + 102 * 16 * MiB
+        self.out = base + 103 * 16 * MiB
+        self.q = base + 104 * 16 * MiB
+        self.scales = base + 105 * 16 * MiB
+        self.eps = 1e-6
+        self.group = 128
+        self.variant = 0
+        self.grid_cap = 0
+
+    def call(self):
+        arr = (ctypes.c_void_p * max(1, len(self.partials)))(*self.partials) if self.partials is not None else None
+        if self.quant:
+            return L.farn_reduce_add_rmsnorm_quant_group_ex(
+                arr, self.R, self.residual, self.gamma, self.eps, self.T, self.H, self.group,
+                self.residual_out, self.out, self.q, self.scales, None, self.variant, self.grid_cap)
+        return L.farn_reduce_add_rmsnorm_ex(arr, self.R, self.residual, self.gamma, self.eps, self.T,
+                                            self.H, self.residual_out, self.out, None, self.variant,
+                                            self.grid_cap)
+
+
+def mk(**kw):
+    quant = kw.pop("quant", False)
+    dims = {k: kw.pop(k) for k in ("R", "T", "H") if k in kw}
+    c = FakeCall(quant=quant, **dims)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+REJECTIONS = [
+    # (description, FakeCall overrides, expected status)
+    ("partials NULL", dict(partials=None), NULL),
+    ("a partial NULL", dict(partials=[0x10_0000_0000, 0]), NULL),
+    ("gamma NULL", dict(gamma=None), NULL),
+    ("residual_out NULL", dict(residual_out=None), NULL),
+    ("plain out NULL", dict(out=None), NULL),
+    ("quant q NULL", dict(quant=True, q=None), NULL),
+    ("quant scales NULL", dict(quant=True, scales=None), NULL),
+    ("R = 0", dict(R=0, partials=[1 << 36]), SHAPE),
+    ("R = 9", dict(R=9), SHAPE),
+    ("T < 0", dict(T=-1), SHAPE),
+    ("T huge", dict(T=1 << 41), SHAPE),
+    ("H = 0", dict(H=0), SHAPE),
+    ("H % 8", dict(H=260), SHAPE),
+    ("H > max", dict(H=F.MAX_H + 8), SHAPE),
+    ("quant group 64", dict(quant=True, group=64), SHAPE),
+    ("quant H % 128", dict(quant=True, H=264), SHAPE),
+    ("eps NaN", dict(eps=float("nan")), EPS),
+    ("eps inf", dict(eps=float("inf")), EPS),
+    ("eps < 0", dict(eps=-1e-6), EPS),
+    ("partial misaligned", dict(partials=[0x10_0000_0000, 0x10_0000_0008 + 16 * MiB]), ALIGN),
+    ("residual misaligned", dict(residual=0x20_0000_0004), ALIGN),
+    ("gamma misaligned", dict(gamma=0x20_0000_0002), ALIGN),
+    ("out misaligned", dict(out=0x20_0000_0008), ALIGN),
+    ("q misaligned", dict(quant=True, q=0x20_0000_0008), ALIGN),
+    ("scales misaligned", dict(quant=True, scales=0x20_0000_0002), ALIGN),
+    ("out overlaps a partial", dict(out=0x10_0000_0000 + 16 * MiB + 256), ALIAS),
+    ("residual_out overlaps gamma", dict(gamma=0x10_0000_0000 + 102 * 16 * MiB + 64), ALIAS),
+    ("out overlaps residual_out", dict(out=0x10_0000_0000 + 102 * 16 * MiB + 1024), ALIAS),
+    ("out == residual (not in place)", dict(out=0x10_0000_0000 + 100 * 16 * MiB), ALIAS),
+    ("residual_out shifted into residual", dict(residual_out=0x10_0000_0000 + 100 * 16 * MiB + 16), ALIAS),
+    ("q overlaps scales", dict(quant=True, scales=0x10_0000_0000 + 104 * 16 * MiB + 512), ALIAS),
+    ("q overlaps a partial", dict(quant=True, q=0x10_0000_0000 + 16), ALIAS),
+    ("variant 3", dict(variant=3), VARIANT),
+    ("variant -1", dict(variant=-1), VARIANT),
+    ("grid_cap < 0", dict(grid_cap=-1), VARIANT),
+]
+
+
+@pytest.mark.parametrize("what,kw,want", REJECTIONS, ids=[r[0] for r in REJECTIONS])
+def test_rejections(what, kw, want):
+    assert mk(**kw).call() == want, what
+
+
+def test_empty_call_enqueues_nothing():
+    # T == 0 passes every check and returns OK without a launch (no GPU needed)
+    assert mk(T=0).call() == OK
+    assert mk(T=0, quant=True).call() == OK
+    assert mk(T=0, residual=None).call() == OK
+
+
+def test_quant_out_may_be_null_and_residual_may_be_null():
+    # these are valid; with T == 0 they are accepted without a launch
+    assert mk(T=0, quant=True, out=None).call() == OK
+    assert mk(T=0, quant=True, residual=None).call() == OK
+
+
+def test_validation_unit_is_hip_free():
+    """The C-ABI layer compiles with plain g++ and no HIP headers."""
+    src = os.path.join(os.path.dirname(F.LIB_PATH), "csrc", "farn_api.cpp")
+    text = open(src).read()
+    assert "hip/" not in text and "hip" not in re.findall(r"#include\s*[<\"]([^>\"]+)", text)
+    subprocess.run(["g++", "-std=c++17", "-fsyntax-only", "-Wall", "-Wextra", "-Werror", src], check=True)

@@ -1,0 +1,290 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element,
+on the same seeded bf16 inputs, at the tolerances stated in tests/parity.py.
+
+Small configurations are compared whole. The full-size prefill chunk (R=8, T=8192,
+H=7168) and the large sweep points are run whole on the GPU, in the launch
+configuration the bench times, and compared on sampled rows (the oracle computes
+rows independently), plus whole-tensor properties.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tp_all_reduce_amd as F
+from gen import CONFIGS, make_inputs, sweep_config
+from parity import compare_bf16, compare_fp8, from_dev_bf16, to_dev_bf16, within_tolerance
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+VARIANTS = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; none is visible")
+    return torch.device("cuda:0")
+
+
+class Uploaded:
+    def __init__(self, d, dev, residual=True):
+        self.d = d
+        self.R, self.T, self.H = d["R"], d["T"], d["H"]
+        self.P = [to_dev_bf16(d["partials"][r], dev) for r in range(self.R)]
+        self.res = to_dev_bf16(d["residual"], dev) if residual else None
+        self.g = to_dev_bf16(d["gamma"], dev)
+
+    def oracle_rows(self, rows, quant, emit_out=True, residual=True):
+        d = self.d
+        P = d["partials"][:, rows, :]
+        res = d["residual"][rows] if (residual and self.res is not None) else None
+        if quant:
+            return oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], EPS, 128, emit_out, nthreads=8)
+        return oracle.reduce_add_rmsnorm(P, res, d["gamma"], EPS, nthreads=8)
+
+
+def run_and_compare(u: Uploaded, quant: bool, variant: str = "auto", grid_cap: int = 0,
+                    emit_out: bool = True, rows=None, label: str = ""):
+    say(f"[gpu] {label} R={u.R} T={u.T} H={u.H} quant={quant} variant={variant} cap={grid_cap} "
+        f"emit={emit_out} residual={u.res is not None}")
+    if quant:
+        ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, emit_out=emit_out,
+                                                          variant=VARIANTS[variant], grid_cap=grid_cap)
+    else:
+        ro, out = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=VARIANTS[variant], grid_cap=grid_cap)
+    torch.cuda.synchronize()
+    rows = np.arange(u.T) if rows is None else np.asarray(rows)
+    g_ro = from_dev_bf16(ro)[rows]
+    g_out = from_dev_bf16(out)[rows] if out is not None else None
+    ref = u.oracle_rows(rows, quant, emit_out)
+    rep_ro = compare_bf16("residual_out", g_ro, ref[0])
+    rep_out = compare_bf16("out", g_out, ref[1]) if g_out is not None else None
+    rep_fp8 = None
+    if quant:
+        rep_fp8 = compare_fp8(q.cpu().numpy()[rows], ref[2], sc.cpu().numpy()[rows], ref[3])
+    ok, why = within_tolerance(rep_ro, rep_out, rep_fp8)
+    assert ok, f"{label}: {why} | {rep_ro} {rep_out} {rep_fp8}"
+    return rep_ro, rep_out, rep_fp8
+
+
+# ------------------------------------------------------------------ the configurations
+SMALL = ["tiny", "decode_ds", "decode_fp8"]
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", SMALL)
+def test_configs_small(dev, name, variant):
+    cfg = CONFIGS[name]
+    u = Uploaded(make_inputs(cfg), dev)
+    for quant in cfg.quant:
+        run_and_compare(u, quant, variant, label=name)
+    if cfg.H % 128 == 0 and True not in cfg.quant:
+        run_and_compare(u, True, variant, label=name + "+fp8")
+
+
+def _sample_rows(T, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 2, T // 2, T - 2, T - 1, 255, 256, 257, 511, 512, 1023, 1024]
+    rows = set(r for r in edge if 0 <= r < T) | set(rng.integers(0, T, n).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.fixture(scope="module")
+def prefill(dev):
+    say("[gpu] generating prefill chunk R=8 T=8192 H=7168")
+    return Uploaded(make_inputs(CONFIGS["prefill"]), dev)
+
+
+@pytest.mark.parametrize("quant", [False, True])
+@pytest.mark.parametrize("variant", ["auto", "latency", "bandwidth"])
+def test_prefill_full_size_sampled(prefill, quant, variant):
+    rows = _sample_rows(prefill.T)
+    run_and_compare(prefill, quant, variant, rows=rows, label="prefill")
+
+
+def test_prefill_full_size_properties(prefill):
+    """Whole-tensor checks at full size: latency and bandwidth paths agree bit for bit on
+    every row, and every output is finite."""
+    say("[gpu] prefill whole-tensor variant identity")
+    a = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_LATENCY)
+    b = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    assert torch.isfinite(a[0].float()).all() and torch.isfinite(a[1].float()).all()
+    assert torch.isfinite(a[3]).all() and (a[3] > 0).all()
+    assert ((a[2] & 0x7F) == 0x7E).view(prefill.T, -1, 128).any(dim=2).all()  # a 448 code per group
+
+
+@pytest.mark.parametrize("T", [2, 8, 64, 256, 1024, 4096])
+def test_sweep_points(dev, T):
+    cfg = sweep_config(T)
+    u = Uploaded(make_inputs(cfg), dev)
+    rows = None if T <= 256 else _sample_rows(T, 32, seed=T)
+    for variant in VARIANTS:
+        run_and_compare(u, False, variant, rows=rows, label=cfg.name)
+
+
+# ------------------------------------------------------------------ edge shapes
+@pytest.mark.parametrize("T", [1, 5, 80, 81])
+def test_edge_T(dev, T):
+    u = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=100 + T, T=T), dev)
+    for variant in VARIANTS:
+        run_and_compare(u, False, variant, label=f"T{T}")
+        run_and_compare(u, True, variant, label=f"T{T}")
+
+
+@pytest.mark.parametrize("H", [8, 16, 64, 264, 512, 1024, 2048, 4096, 7168, 8192, 8200, 16384, 24576, 32768])
+def test_edge_H(dev, H):
+    u = Uploaded(make_inputs(CONFIGS["tiny"], seed=H, R=3, T=6, H=H), dev)
+    for variant in VARIANTS:
+        run_and_compare(u, False, variant, label=f"H{H}")
+        if H % 128 == 0:
+            run_and_compare(u, True, variant, label=f"H{H}")
+
+
+@pytest.mark.parametrize("R", list(range(1, 9)))
+def test_edge_R(dev, R):
+    u = Uploaded(make_inputs(CONFIGS["tiny"], seed=R, R=R, T=7, H=1024), dev)
+    for variant in ("latency", "bandwidth"):
+        run_and_compare(u, False, variant, label=f"R{R}")
+        run_and_compare(u, True, variant, label=f"R{R}")
+
+
+def test_no_residual(dev):
+    d = make_inputs(CONFIGS["decode_fp8"], seed=7)
+    u = Uploaded(d, dev, residual=False)
+    for variant in VARIANTS:
+        run_and_compare(u, False, variant, label="nores")
+        run_and_compare(u, True, variant, label="nores")
+    # R=1 without residual: residual_out is P_0 bit for bit
+    u1 = Uploaded(make_inputs(CONFIGS["tiny"], seed=8, R=1, T=9, H=2048), dev, residual=False)
+    ro, _ = F.reduce_add_rmsnorm(u1.P, None, u1.g, EPS)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bf16(ro), u1.d["partials"][0])
+
+
+def test_quant_without_bf16_out(dev):
+    u = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=9), dev)
+    for variant in VARIANTS:
+        run_and_compare(u, True, variant, emit_out=False, label="no-out")
+
+
+def test_in_place_residual(dev):
+    d = make_inputs(CONFIGS["decode_ds"], seed=10, T=33)
+    ref_ro, ref_out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
+    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+        say(f"[gpu] in-place residual variant={variant}")
+        u = Uploaded(d, dev)
+        ro, out = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, residual_out=u.res, variant=variant)
+        torch.cuda.synchronize()
+        assert ro.data_ptr() == u.res.data_ptr()
+        assert np.array_equal(from_dev_bf16(ro), ref_ro)
+        ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro), ref_ro),
+                                   compare_bf16("out", from_dev_bf16(out), ref_out), None)
+        assert ok, why
+
+
+def test_empty_T(dev):
+    say("[gpu] T = 0")
+    p = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    g = torch.ones(256, dtype=torch.bfloat16, device=dev)
+    ro, out = F.reduce_add_rmsnorm([p, p], p, g, EPS)
+    ro, out, q, s = F.reduce_add_rmsnorm_quant_group([p], None, g, EPS)
+    torch.cuda.synchronize()
+    assert ro.numel() == 0 and q.numel() == 0
+
+
+# ------------------------------------------------------------------ state, order, determinism
+@pytest.mark.parametrize("cap", [1, 2, 3, 7])
+def test_bandwidth_small_grid_reuses_lds(dev, cap):
+    """A tiny grid makes each workgroup stream many rows through its two LDS slots and two
+    register sets; a missing barrier or a slot reused too early shows up as wrong rows."""
+    u = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=20 + cap, T=61), dev)
+    run_and_compare(u, False, "bandwidth", grid_cap=cap, label="cap")
+    run_and_compare(u, True, "bandwidth", grid_cap=cap, label="cap")
+
+
+def test_back_to_back_calls_do_not_leak(dev):
+    """Alternate two shapes on one stream without synchronising and check every result."""
+    say("[gpu] back-to-back alternating calls")
+    ua = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=30), dev)
+    ub = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=31), dev)
+    outs = []
+    for i in range(6):
+        if i % 2 == 0:
+            outs.append(("a", F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS, variant=i % 3)))
+        else:
+            outs.append(("b", F.reduce_add_rmsnorm_quant_group(ub.P, ub.res, ub.g, EPS, variant=i % 3)))
+    torch.cuda.synchronize()
+    ref_a = ua.oracle_rows(np.arange(ua.T), False)
+    ref_b = ub.oracle_rows(np.arange(ub.T), True)
+    for tag, res in outs:
+        if tag == "a":
+            ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(res[0]), ref_a[0]),
+                                       compare_bf16("out", from_dev_bf16(res[1]), ref_a[1]), None)
+        else:
+            ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(res[0]), ref_b[0]),
+                                       compare_bf16("out", from_dev_bf16(res[1]), ref_b[1]),
+                                       compare_fp8(res[2].cpu().numpy(), ref_b[2], res[3].cpu().numpy(), ref_b[3]))
+        assert ok, why
+
+
+def test_deterministic_and_variants_identical(dev):
+    u = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=40, T=200), dev)
+    say("[gpu] determinism")
+    runs = [F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=v, grid_cap=c)
+            for v, c in ((1, 0), (1, 0), (2, 0), (2, 5))]
+    torch.cuda.synchronize()
+    for other in runs[1:]:
+        for x, y in zip(runs[0], other):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+# ------------------------------------------------------------------ special values
+def test_subnormal_and_tiny_values(dev):
+    """Sums in the bf16 subnormal range: residual_out must round exactly like the oracle
+    (no flush to zero)."""
+    d = make_inputs(CONFIGS["tiny"], seed=50, R=4, T=4, H=512)
+    P = d["partials"].astype(np.uint32)
+    # move every exponent down so that values sit around 2^-128 .. 2^-120
+    exp = (P >> 7) & 0xFF
+    newexp = np.clip(exp.astype(np.int32) - 122, 0, 255).astype(np.uint32)
+    P = np.where(exp > 0, (P & 0x807F) | (newexp << 7), P).astype(np.uint16)
+    d["partials"] = P
+    d["residual"] = np.zeros_like(d["residual"])
+    u = Uploaded(d, dev)
+    for variant in ("latency", "bandwidth"):
+        run_and_compare(u, False, variant, label="subnormal")
+        run_and_compare(u, True, variant, label="subnormal")
+
+
+def test_nan_row(dev):
+    d = make_inputs(CONFIGS["tiny"], seed=60, R=2, T=4, H=256)
+    d["partials"][1, 2, 5] = 0x7FC0
+    u = Uploaded(d, dev)
+    say("[gpu] NaN row")
+    ro, out, q, s = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS)
+    torch.cuda.synchronize()
+    rof = ro.float().cpu().numpy()
+    outf = out.float().cpu().numpy()
+    assert np.isnan(rof[2, 5]) and np.isfinite(np.delete(rof[2], 5)).all()
+    assert np.isnan(outf[2]).all() and np.isfinite(outf[[0, 1, 3]]).all()
+    qq = q.cpu().numpy()
+    assert ((qq[2] & 0x7F) == 0x7F).all() and np.isnan(s.cpu().numpy()[2]).all()
+    ref = u.oracle_rows(np.array([0, 1, 3]), True)
+    ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro)[[0, 1, 3]], ref[0]),
+                               compare_bf16("out", from_dev_bf16(out)[[0, 1, 3]], ref[1]),
+                               compare_fp8(qq[[0, 1, 3]], ref[2], s.cpu().numpy()[[0, 1, 3]], ref[3]))
+    assert ok, why

@@ -1,0 +1,157 @@
+"""Python binding of libfarn.so: fused reduce + residual-add + RMSNorm (+ per-group FP8
+quant) for MI355X (gfx950).
+
+Argument marshalling only: torch tensors supply device memory and the stream; every
+step of the op runs in the HIP kernels behind the C ABI (include/farn.h). Importing
+this package loads the in-tree library and raises if it has not been built; there
+is no fallback.
+
+The op is the per-GPU body of the fused tensor-parallel all-reduce + RMSNorm of
+"ROCm AITER fused all-reduce + RMSNorm" (vLLM #37646 summary, fused_ar_rms) and of
+the per-group FP8 variant in "AMD fused AllReduce-RMSNorm quant kernel" (sglang
+#24651 summary, tensor_model_parallel_fused_allreduce_rmsnorm_quant_per_group).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfarn.so")
+
+OK = 0
+STATUS = {0: "FARN_OK", 1: "FARN_ERR_NULL", 2: "FARN_ERR_SHAPE", 3: "FARN_ERR_ALIGN",
+          4: "FARN_ERR_ALIAS", 5: "FARN_ERR_EPS", 6: "FARN_ERR_LAUNCH", 7: "FARN_ERR_VARIANT"}
+VARIANT_AUTO, VARIANT_LATENCY, VARIANT_BANDWIDTH = 0, 1, 2
+MAX_R, MAX_H, GROUP = 8, 32768, 128
+EXPORTS = ("farn_reduce_add_rmsnorm", "farn_reduce_add_rmsnorm_quant_group",
+           "farn_reduce_add_rmsnorm_ex", "farn_reduce_add_rmsnorm_quant_group_ex",
+           "farn_select_variant", "farn_status_string", "farn_abi_version")
+
+
+class FarnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib.farn_status_string(status).decode()})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m tp_all_reduce_amd.build` "
+                          "(hipcc, gfx950). There is no fallback path.")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    base = [pp, i32, vp, vp, f32, i64, i64]
+    L.farn_reduce_add_rmsnorm.argtypes = base + [vp, vp, vp]
+    L.farn_reduce_add_rmsnorm_quant_group.argtypes = base + [i32, vp, vp, vp, vp, vp]
+    L.farn_reduce_add_rmsnorm_ex.argtypes = base + [vp, vp, vp, i32, i32]
+    L.farn_reduce_add_rmsnorm_quant_group_ex.argtypes = base + [i32, vp, vp, vp, vp, vp, i32, i32]
+    for fn in EXPORTS[:4]:
+        getattr(L, fn).restype = i32
+    L.farn_select_variant.argtypes = [i32, i64, i64, i32]
+    L.farn_select_variant.restype = i32
+    L.farn_status_string.argtypes = [i32]
+    L.farn_status_string.restype = ctypes.c_char_p
+    L.farn_abi_version.argtypes = []
+    L.farn_abi_version.restype = i32
+    return L
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def abi_version() -> int:
+    return _lib.farn_abi_version()
+
+
+def select_variant(R: int, T: int, H: int, quant: bool) -> int:
+    return _lib.farn_select_variant(R, T, H, int(bool(quant)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _check_bf16(name, t, shape, device):
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"{name}: expected contiguous bfloat16 {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual_out=None,
+                       out=None, variant: int = VARIANT_AUTO, grid_cap: int = 0, stream=None):
+    """Sum the R partials (list of bf16 [T,H] device tensors) in rank order in fp32, add the
+    residual (or None), round to bf16 -> residual_out, then RMSNorm with gamma -> out.
+    residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
+    p0 = partials[0]
+    T, H = p0.shape
+    dev = p0.device
+    for i, p in enumerate(partials):
+        _check_bf16(f"partials[{i}]", p, (T, H), dev)
+    if residual is not None:
+        _check_bf16("residual", residual, (T, H), dev)
+    _check_bf16("gamma", gamma, (H,), dev)
+    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    out = torch.empty_like(p0) if out is None else out
+    _check_bf16("residual_out", residual_out, (T, H), dev)
+    _check_bf16("out", out, (T, H), dev)
+    st = _lib.farn_reduce_add_rmsnorm_ex(
+        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
+        _ptr(residual_out), _ptr(out), _stream(dev, stream), variant, grid_cap)
+    if st != OK:
+        raise FarnError(st, "farn_reduce_add_rmsnorm")
+    return residual_out, out
+
+
+def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6, *,
+                                   group_size: int = GROUP, emit_out: bool = True, residual_out=None,
+                                   out=None, q=None, scales=None, variant: int = VARIANT_AUTO,
+                                   grid_cap: int = 0, stream=None):
+    """The plain call, then per-128-channel E4M3 quant of the bf16 output. Returns
+    (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128])."""
+    p0 = partials[0]
+    T, H = p0.shape
+    dev = p0.device
+    for i, p in enumerate(partials):
+        _check_bf16(f"partials[{i}]", p, (T, H), dev)
+    if residual is not None:
+        _check_bf16("residual", residual, (T, H), dev)
+    _check_bf16("gamma", gamma, (H,), dev)
+    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    if emit_out and out is None:
+        out = torch.empty_like(p0)
+    if not emit_out:
+        out = None
+    q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
+    G = H // group_size if group_size > 0 else 0
+    scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn) or q.numel() != T * H or not q.is_contiguous():
+        raise ValueError("q: expected contiguous uint8 / float8_e4m3fn [T, H]")
+    if scales.dtype != torch.float32 or scales.numel() != T * G or not scales.is_contiguous():
+        raise ValueError("scales: expected contiguous float32 [T, H/group_size]")
+    st = _lib.farn_reduce_add_rmsnorm_quant_group_ex(
+        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
+        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant, grid_cap)
+    if st != OK:
+        raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
+    return residual_out, out, q, scales

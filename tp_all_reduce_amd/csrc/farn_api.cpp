@@ -1,0 +1,191 @@
+// C-ABI entry points: argument checks on the host, variant choice, then one launch.
+// This file makes no HIP call; every check runs before anything is enqueued, so a
+// rejected call leaves the stream untouched (the analogue of the pages' fused path
+// returning None so the caller falls back: "AMD fused AllReduce-RMSNorm quant
+// kernel", sglang #24651 summary, layernorm.py snippet).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/farn.h"
+#include "farn_internal.h"
+
+namespace farn {
+
+RowShape row_shape(int64_t H) {
+    const int64_t nvec = H / 8;
+    RowShape s;
+    if (nvec <= 1024) {
+        s.lanes = (int)(((nvec + 63) / 64) * 64);
+        s.vpl = 1;
+    } else if (nvec <= 2048) {
+        s.lanes = 1024;
+        s.vpl = 2;
+    } else {
+        s.lanes = 1024;
+        s.vpl = 4;
+    }
+    return s;
+}
+
+}  // namespace farn
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Range range_of(const void *p, int64_t bytes) {
+    uintptr_t lo = (uintptr_t)p;
+    return Range{lo, lo + (uintptr_t)bytes};
+}
+
+// Full check of one call. quant = true for the FP8 call.
+farn_status check(const void *const *partials, int R, const void *residual, const void *gamma,
+                  float eps, int64_t T, int64_t H, int group_size, bool quant, void *residual_out,
+                  void *out, void *q, float *scales) {
+    if (R < 1 || R > FARN_MAX_R) return FARN_ERR_SHAPE;
+    if (T < 0 || T > ((int64_t)1 << 40) || H <= 0 || H % 8 != 0 || H > FARN_MAX_H)
+        return FARN_ERR_SHAPE;
+    if (quant && (group_size != FARN_GROUP || H % FARN_GROUP != 0)) return FARN_ERR_SHAPE;
+    if (!(eps >= 0.0f) || isinf(eps)) return FARN_ERR_EPS;
+    if (!partials || !gamma) return FARN_ERR_NULL;
+    if (T == 0) return FARN_OK;  // no row buffer is touched; empty tensors may have NULL data
+    for (int r = 0; r < R; ++r)
+        if (!partials[r]) return FARN_ERR_NULL;
+    if (!residual_out) return FARN_ERR_NULL;
+    if (quant) {
+        if (!q || !scales) return FARN_ERR_NULL;
+    } else if (!out) {
+        return FARN_ERR_NULL;
+    }
+
+    auto a16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+    for (int r = 0; r < R; ++r)
+        if (!a16(partials[r])) return FARN_ERR_ALIGN;
+    if ((residual && !a16(residual)) || !a16(gamma) || !a16(residual_out) || (out && !a16(out)))
+        return FARN_ERR_ALIGN;
+    if (quant && (!a16(q) || ((uintptr_t)scales & 3u) != 0)) return FARN_ERR_ALIGN;
+
+    const int64_t tile = T * H * 2;
+    Range ins[FARN_MAX_R + 2];
+    int n_in = 0;
+    for (int r = 0; r < R; ++r) ins[n_in++] = range_of(partials[r], tile);
+    ins[n_in++] = range_of(gamma, H * 2);
+    Range res_in = residual ? range_of(residual, tile) : Range{0, 0};
+
+    Range outs[4];
+    int n_out = 0;
+    outs[n_out++] = range_of(residual_out, tile);
+    if (out) outs[n_out++] = range_of(out, tile);
+    if (quant) {
+        outs[n_out++] = range_of(q, T * H);
+        outs[n_out++] = range_of(scales, T * (H / FARN_GROUP) * 4);
+    }
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j)
+            if (overlaps(outs[i], ins[j])) return FARN_ERR_ALIAS;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(outs[i], outs[j])) return FARN_ERR_ALIAS;
+        if (residual && overlaps(outs[i], res_in)) {
+            const bool in_place = (i == 0 && residual_out == residual);
+            if (!in_place) return FARN_ERR_ALIAS;
+        }
+    }
+    return FARN_OK;
+}
+
+// AUTO rule: the latency path (one workgroup per row) while the rows do not fill the
+// chip several times over; the persistent bandwidth path beyond that.
+int select(int R, int64_t T, int64_t H, int quant) {
+    (void)R;
+    (void)H;
+    (void)quant;
+    return T <= 512 ? FARN_VARIANT_LATENCY : FARN_VARIANT_BANDWIDTH;
+}
+
+farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
+                float eps, int64_t T, int64_t H, int group_size, bool quant, void *residual_out,
+                void *out, void *q, float *scales, void *stream, int variant, int grid_cap) {
+    if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH || grid_cap < 0)
+        return FARN_ERR_VARIANT;
+    farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
+                           residual_out, out, q, scales);
+    if (st != FARN_OK || T == 0) return st;
+    if (variant == FARN_VARIANT_AUTO) variant = select(R, T, H, quant ? 1 : 0);
+    if (variant == FARN_VARIANT_LATENCY && T > INT32_MAX) return FARN_ERR_SHAPE;
+    farn::Call c;
+    for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
+    c.R = R;
+    c.residual = residual;
+    c.gamma = gamma;
+    c.eps = eps;
+    c.T = T;
+    c.H = H;
+    c.residual_out = residual_out;
+    c.out = out;
+    c.q = quant ? q : nullptr;
+    c.scales = quant ? scales : nullptr;
+    c.stream = stream;
+    return farn::launch(c, variant, grid_cap) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,
+                                    const void *gamma, float eps, int64_t T, int64_t H,
+                                    void *residual_out, void *out, void *stream) {
+    return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
+               nullptr, stream, FARN_VARIANT_AUTO, 0);
+}
+
+farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int R,
+                                                const void *residual, const void *gamma, float eps,
+                                                int64_t T, int64_t H, int group_size,
+                                                void *residual_out, void *out, void *q,
+                                                float *scales, void *stream) {
+    return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
+               scales, stream, FARN_VARIANT_AUTO, 0);
+}
+
+farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
+                                       const void *gamma, float eps, int64_t T, int64_t H,
+                                       void *residual_out, void *out, void *stream, int variant,
+                                       int grid_cap) {
+    return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
+               nullptr, stream, variant, grid_cap);
+}
+
+farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, int R,
+                                                   const void *residual, const void *gamma,
+                                                   float eps, int64_t T, int64_t H, int group_size,
+                                                   void *residual_out, void *out, void *q,
+                                                   float *scales, void *stream, int variant,
+                                                   int grid_cap) {
+    return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
+               scales, stream, variant, grid_cap);
+}
+
+int farn_select_variant(int R, int64_t T, int64_t H, int quant) { return select(R, T, H, quant); }
+
+const char *farn_status_string(int status) {
+    switch (status) {
+        case FARN_OK: return "ok";
+        case FARN_ERR_NULL: return "a required pointer is NULL";
+        case FARN_ERR_SHAPE: return "unsupported shape (R, T, H or group size)";
+        case FARN_ERR_ALIGN: return "a buffer is not aligned (16 bytes; scales 4 bytes)";
+        case FARN_ERR_ALIAS: return "an output overlaps an input or another output";
+        case FARN_ERR_EPS: return "eps is not finite or is negative";
+        case FARN_ERR_LAUNCH: return "kernel launch failed";
+        case FARN_ERR_VARIANT: return "unknown variant or negative grid cap";
+        default: return "unknown status";
+    }
+}
+
+int farn_abi_version(void) { return FARN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Internal interface between the C-ABI layer (argument checks, variant choice)
+// and the HIP kernels. Not installed; callers use include/farn.h.
+#pragma once
+
+#include <stdint.h>
+
+namespace farn {
+
+// One validated call, raw device pointers. q / scales are null for the plain call.
+struct Call {
+    const void *partials[8];
+    int R;
+    const void *residual;  // null: no residual
+    const void *gamma;
+    float eps;
+    int64_t T, H;
+    void *residual_out;
+    void *out;     // null only for the quant call with the bf16 output off
+    void *q;       // quant call only
+    float *scales; // quant call only
+    void *stream;
+};
+
+// Lanes per token row and 16-byte vectors per lane for hidden size H. Both kernel
+// variants use this mapping, so they reduce each row in the same order.
+struct RowShape {
+    int lanes;  // multiple of 64, <= 1024
+    int vpl;    // vectors per lane: 1, 2 or 4
+};
+RowShape row_shape(int64_t H);
+
+// Enqueue the kernel. variant: 1 = latency, 2 = bandwidth (already resolved from AUTO).
+// Returns 0 on success, nonzero when the launch failed.
+int launch(const Call &c, int variant, int grid_cap);
+
+}  // namespace farn

@@ -1,0 +1,451 @@
+// HIP kernels for gfx950 (CDNA4): fused reduce of R rank partials + residual add +
+// RMSNorm (+ per-128-channel E4M3 quant), one token row at a time.
+//
+// The op is the per-GPU body of the fused tensor-parallel all-reduce + RMSNorm of
+// "ROCm AITER fused all-reduce + RMSNorm" (vLLM #37646 summary: all-reduce, then
+// rms_norm of its output, both returned) and of the per-group FP8 variant in "AMD
+// fused AllReduce-RMSNorm quant kernel" (sglang #24651 summary: group_size 128,
+// quant of the bf16 normalised output). Here the R partial buffers sit in local HBM.
+//
+// Work mapping (both variants):
+//   A token row of H bf16 is NV = H/8 16-byte vectors. The row is spread over L
+//   lanes (L = multiple of 64, <= 1024) with VPL vectors per lane, lane-strided:
+//   lane l holds vectors l, l+L, l+2L, ... So every load instruction of a wave is
+//   64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is exactly 16
+//   consecutive lanes (one DPP row) of one vector slot.
+//   Per lane: all R+1 loads of a vector are issued before any is consumed; the
+//   partials are summed in fp32 in rank order, the residual added last, the sum
+//   rounded to bf16 (residual_out) and kept packed in registers. The sum of squares
+//   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
+//   per wave through LDS -> every wave adds the per-wave values in wave order; the
+//   normalisation product is fp64 too, rounded once to bf16. The row never passes
+//   through LDS; only one double per wave does.
+//   The order of that reduction depends only on (H, L, VPL), which both variants
+//   share, so both give bit-identical results.
+//
+// Variants:
+//   latency   - one workgroup per row (grid = T). Every wave issues its loads at once;
+//               used while T is small (decode).
+//   bandwidth - persistent: grid = resident workgroups; each streams rows t, t+G, ...
+//               and issues the loads of its next row before reducing the current
+//               one, so each CU always has a row of loads in flight (prefill).
+//
+// No MFMA: nothing here is a contraction; the op is HBM-bound (about 0.5 flop per
+// byte against a ridge of ~20 flop/byte).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "farn_internal.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+struct Params {
+    const void *p[8];   // rank partials, bf16 [T,H]
+    const void *res;    // residual or null
+    const void *gamma;  // [H]
+    void *res_out;
+    void *out;          // null: bf16 output not written (quant call only)
+    void *q;            // E4M3 codes [T,H] (quant only)
+    float *scales;      // [T, H/128] (quant only)
+    int64_t T;
+    int nvec;           // H / 8
+    int ngroups;        // H / 128
+    double h;           // H (mean divisor)
+    float eps;
+};
+
+constexpr int kMaxWaves = 16;
+
+// ---------------------------------------------------------------- buffer access
+// Every global access goes through a buffer resource covering exactly one row of one
+// array. The hardware range check turns a load past the end of the row (lanes beyond
+// H/8, or a row >= T, whose resource has 0 records) into zeros and drops such a store,
+// so no access needs a branch: the loads of a row are issued straight-line and the
+// compiler's vmcnt bookkeeping stays exact across the software pipeline.
+// dword3 0x00020000: 32-bit data format, the raw-buffer setting for CDNA.
+constexpr int kRsrcFlags = 0x00020000;
+constexpr int kNT = 2;  // cache policy: non-temporal (streamed once)
+constexpr uint32_t kDropOffset = 0x80000000u;  // beyond any row: store dropped
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void *base, int64_t byte_off, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + byte_off), (short)0,
+                                             nbytes, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
+}
+__device__ __forceinline__ void st16(u32x4 v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNT);
+}
+__device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kNT);
+}
+__device__ __forceinline__ void st4(float v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------- number formats
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = bf16x2{(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp64 -> fp32 rounded to odd: truncate toward zero, then set the last bit if anything
+// was dropped. A value rounded to odd with 24 bits and then to nearest-even with 8 bits
+// lands where one direct rounding to 8 bits would, so fp64 -> bf16 rounds once.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    const float f = (float)d;  // nearest even
+    const double back = (double)f;
+    if (back == d) return f;
+    uint32_t b = __float_as_uint(f);
+    if (__builtin_fabs(back) > __builtin_fabs(d)) b -= 1u;  // rounded away from zero: step back
+    return __uint_as_float(b | 1u);
+}
+
+// Two fp64 -> packed bf16 pair, each rounded once to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_d(double lo, double hi) {
+    return pack_bf16(f64_to_f32_odd(lo), f64_to_f32_odd(hi));
+}
+
+// OCP E4M3 code of the exact quotient o / scale (scale > 0), rounded once to nearest
+// even, saturating to +-448. Written from the format definition: 3 mantissa bits kept
+// from the binary32 pattern with round-to-nearest on the dropped 20 bits, exponent
+// rebiased from 127 to 7; below 2^-6 the grid is 2^-9.
+// The fp32 quotient qv = fl32(o/scale) can sit exactly on an E4M3 midpoint while the
+// exact quotient does not (o and scale have few significant bits, so such ratios are
+// common); rounding qv there would round twice. rem = o - qv*scale is exact in one FMA
+// for a correctly rounded quotient, and its sign says on which side of qv the exact
+// quotient lies: on a midpoint that side decides, and only an exact tie goes to even.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float o, float scale) {
+    const float qv = o / scale;
+    const float rem = __builtin_fmaf(-qv, scale, o);
+    const uint32_t u = __float_as_uint(qv);
+    const uint32_t s = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    const bool exact = rem == 0.0f;
+    const bool above = (rem > 0.0f) == (qv > 0.0f);  // exact magnitude above |qv|
+    if (a > 0x7f800000u) return s | 0x7fu;   // NaN
+    if (a >= 0x43e00000u) return s | 0x7eu;  // |v| >= 448 (incl. inf): largest finite
+    if (a < 0x3c800000u) {                   // |v| < 2^-6: subnormal grid m * 2^-9
+        const float m = __uint_as_float(a) * 512.0f;  // exact scaling
+        const float fl = __builtin_floorf(m);
+        const bool tie = (m - fl) == 0.5f;
+        const float r = (tie && !exact) ? fl + (above ? 1.0f : 0.0f) : __builtin_rintf(m);
+        return s | (uint32_t)r;              // 0..8; 8 is the code of 2^-6
+    }
+    const bool tie = (a & 0xfffffu) == 0x80000u;
+    const uint32_t bias = (tie && !exact) ? (above ? 0x80000u : 0x7ffffu) : 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t c = ((a + bias) >> 20) - (120u << 3);  // E8 M3 rounded, rebias 127 -> 7
+    return s | (c > 0x7eu ? 0x7eu : c);
+}
+
+// ---------------------------------------------------------------- cross-lane
+// DPP controls (gfx9): quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140. After the four steps every lane of a
+// 16-lane row holds the row's total, identical in every lane (each step adds the
+// same pair in both lanes, and fp32 addition is commutative).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Max of non-negative float bit patterns as unsigned integers: orders every finite
+// value and inf, and a NaN (above inf) wins, so NaN propagates into the scale.
+__device__ __forceinline__ uint32_t row16_umax(uint32_t x) {
+    x = max(x, dpp_u<0xB1>(x));
+    x = max(x, dpp_u<0x4E>(x));
+    x = max(x, dpp_u<0x141>(x));
+    x = max(x, dpp_u<0x140>(x));
+    return x;
+}
+
+// fp64 through DPP: the two 32-bit halves move with the same control.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = dpp_u<CTRL>((uint32_t)u);
+    const uint32_t hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ double row16_sum_d(double x) {
+    x = x + dpp_d<0xB1>(x);
+    x = x + dpp_d<0x4E>(x);
+    x = x + dpp_d<0x141>(x);
+    x = x + dpp_d<0x140>(x);
+    return x;
+}
+
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Wave total: the four 16-lane row totals, read as scalars and added in a fixed order.
+__device__ __forceinline__ double wave_sum_d(double x) {
+    x = row16_sum_d(x);
+    return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
+}
+
+// ---------------------------------------------------------------- one row
+// The loads of one vector slot: R partials and the residual (zeros when absent).
+template <int R>
+struct SlotIn {
+    u32x4 p[R];
+    u32x4 res;
+};
+
+// Issue the R+1 loads of slot byte offset `off` of row t. A row t >= T loads zeros.
+template <int R>
+__device__ __forceinline__ void load_slot(SlotIn<R> &in, const Params &k, int64_t t, uint32_t off) {
+    const int rb = t < k.T ? k.nvec * 16 : 0;
+    const int64_t ro = t * (int64_t)k.nvec * 16;
+#pragma unroll
+    for (int r = 0; r < R; ++r) in.p[r] = ld16(row_rsrc(k.p[r], ro, rb), off);
+    in.res = ld16(row_rsrc(k.res, k.res ? ro : 0, k.res ? rb : 0), off);
+}
+
+// fp32 sum of the partials in rank order, residual last (skipped, not a +0, when there
+// is none), rounded to bf16 and stored as residual_out; accumulates the squares of the
+// rounded values into ss (fp64). Lanes past the row end see zeros and add nothing.
+template <int R>
+__device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
+                                             uint32_t off, double &ss) {
+    const bool has_res = k.res != nullptr;
+    u32x4 packed;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        float lo = bf_lo(in.p[0][w]);
+        float hi = bf_hi(in.p[0][w]);
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            lo = lo + bf_lo(in.p[r][w]);
+            hi = hi + bf_hi(in.p[r][w]);
+        }
+        const float lo_r = lo + bf_lo(in.res[w]);
+        const float hi_r = hi + bf_hi(in.res[w]);
+        packed[w] = pack_bf16(has_res ? lo_r : lo, has_res ? hi_r : hi);
+    }
+    st16(packed, ro_out, off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const double a = (double)bf_lo(packed[w]);
+        const double b = (double)bf_hi(packed[w]);
+        ss = __builtin_fma(a, a, ss);  // bf16 squares are exact in fp64
+        ss = __builtin_fma(b, b, ss);
+    }
+    return packed;
+}
+
+// Row statistics in fp64: wave DPP tree, one double per wave through `slot` (kMaxWaves
+// doubles), then every wave adds the per-wave values in wave order; rstd =
+// 1/sqrt(ss/H + eps) with correctly rounded fp64 division and square root. The
+// kernel is HBM-bound with ample ALU to spare, and fp64 statistics put `out` on the
+// bf16 value the exact statistics give (an fp32 tree moves about one element in 10^4
+// by one bf16 step, and when that element is a group's amax its scale moves by up to
+// 2^-7). Callers alternate two slots between consecutive rows, so one barrier per row
+// suffices.
+__device__ __forceinline__ double row_rstd(double ss, const Params &k, double *slot) {
+    const int lane = (int)threadIdx.x & 63;
+    const int wave = (int)threadIdx.x >> 6;
+    const int nwaves = (int)blockDim.x >> 6;
+    const double wsum = wave_sum_d(ss);
+    if (lane == 0) slot[wave] = wsum;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < nwaves; ++i) tot = tot + slot[i];
+    return 1.0 / __builtin_sqrt(tot / (double)k.h + (double)k.eps);
+}
+
+// Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16), store
+// out, and (QUANT) its E4M3 codes and group scale.
+template <bool QUANT>
+__device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out,
+                                           rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
+    float o[8];
+    u32x4 packed;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const double lo = (double)bf_lo(yb[w]) * rstd * (double)bf_lo(gam[w]);
+        const double hi = (double)bf_hi(yb[w]) * rstd * (double)bf_hi(gam[w]);
+        packed[w] = pack_bf16_d(lo, hi);
+        o[2 * w] = bf_lo(packed[w]);
+        o[2 * w + 1] = bf_hi(packed[w]);
+    }
+    st16(packed, r_out, off);
+    if constexpr (QUANT) {
+        uint32_t amax = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
+        amax = row16_umax(amax);  // 16 lanes = one 128-channel group
+        const float scale = __uint_as_float(amax) / 448.0f;
+        uint32_t c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = scale == 0.0f ? 0u : e4m3_of_quotient(o[e], scale);
+        u32x2 codes;
+        codes[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        st8(codes, r_q, off >> 1);
+        // one lane per group writes the scale; the others aim past the row (dropped)
+        const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? (off >> 8) * 4u : kDropOffset;
+        st4(scale, r_sc, soff);
+    }
+}
+
+// Whole row t with the loads of slot 0 already issued into `in0` (VPL > 1 loads and
+// reduces the other slots one after the other, to bound register use).
+template <int R, int VPL, bool QUANT>
+__device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
+                                       const Params &k, int64_t t, double *slot) {
+    const uint32_t L16 = blockDim.x * 16u;
+    const uint32_t off0 = threadIdx.x * 16u;
+    const int rb = k.nvec * 16;
+    const int64_t ro = t * (int64_t)rb;
+    const rsrc_t r_ro = row_rsrc(k.res_out, ro, rb);
+    double ss = 0.0;
+    u32x4 yb[VPL];
+    yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
+#pragma unroll
+    for (int v = 1; v < VPL; ++v) {
+        SlotIn<R> in;
+        load_slot<R>(in, k, t, off0 + v * L16);
+        yb[v] = reduce_slot<R>(in, k, r_ro, off0 + v * L16, ss);
+    }
+    const double rstd = row_rstd(ss, k, slot);
+    const rsrc_t r_out = row_rsrc(k.out, k.out ? ro : 0, k.out ? rb : 0);
+    const rsrc_t r_q = row_rsrc(k.q, QUANT ? t * (int64_t)k.nvec * 8 : 0, QUANT ? k.nvec * 8 : 0);
+    const rsrc_t r_sc = row_rsrc(k.scales, QUANT ? t * (int64_t)k.ngroups * 4 : 0,
+                                 QUANT ? k.ngroups * 4 : 0);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) store_slot<QUANT>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16);
+}
+
+template <int VPL>
+__device__ __forceinline__ void load_gamma(u32x4 (&gam)[VPL], const Params &k) {
+    const rsrc_t rg = row_rsrc(k.gamma, 0, k.nvec * 16);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) gam[v] = ld16(rg, (v * blockDim.x + threadIdx.x) * 16u);
+}
+
+// ---------------------------------------------------------------- kernels
+template <int R, int VPL, bool QUANT>
+__global__ __launch_bounds__(1024) void farn_latency(const Params k) {
+    __shared__ double slot[kMaxWaves];
+    const int64_t t = blockIdx.x;
+    SlotIn<R> in;
+    load_slot<R>(in, k, t, threadIdx.x * 16u);
+    u32x4 gam[VPL];
+    load_gamma<VPL>(gam, k);
+    do_row<R, VPL, QUANT>(in, gam, k, t, slot);
+}
+
+template <int R, int VPL, bool QUANT>
+__global__ __launch_bounds__(1024) void farn_bandwidth(const Params k) {
+    __shared__ double slots[2][kMaxWaves];
+    const int64_t G = gridDim.x;
+    int64_t t = blockIdx.x;
+    if (t >= k.T) return;
+    u32x4 gam[VPL];
+    load_gamma<VPL>(gam, k);
+    const uint32_t off0 = threadIdx.x * 16u;
+    SlotIn<R> a, b;
+    load_slot<R>(a, k, t, off0);
+    // Two register sets, alternated by hand so neither is copied (a copy would wait for
+    // the loads in flight): the first slot of row t+G loads while row t finishes. The
+    // prefetch past the last row has 0 records and moves no data.
+    while (true) {
+        load_slot<R>(b, k, t + G, off0);
+        do_row<R, VPL, QUANT>(a, gam, k, t, slots[0]);
+        t += G;
+        if (t >= k.T) break;
+        load_slot<R>(a, k, t + G, off0);
+        do_row<R, VPL, QUANT>(b, gam, k, t, slots[1]);
+        t += G;
+        if (t >= k.T) break;
+    }
+}
+
+// ---------------------------------------------------------------- dispatch tables
+typedef void (*KernelFn)(const Params);
+
+template <int R, bool Q>
+struct Row {
+    static constexpr KernelFn lat[3] = {farn_latency<R, 1, Q>, farn_latency<R, 2, Q>,
+                                        farn_latency<R, 4, Q>};
+    static constexpr KernelFn bw[3] = {farn_bandwidth<R, 1, Q>, farn_bandwidth<R, 2, Q>,
+                                       farn_bandwidth<R, 4, Q>};
+};
+
+template <bool Q>
+KernelFn pick(int variant, int R, int vi) {
+    switch (R) {
+#define FARN_CASE(n) \
+    case n: return variant == 1 ? Row<n, Q>::lat[vi] : Row<n, Q>::bw[vi];
+        FARN_CASE(1) FARN_CASE(2) FARN_CASE(3) FARN_CASE(4)
+        FARN_CASE(5) FARN_CASE(6) FARN_CASE(7) FARN_CASE(8)
+#undef FARN_CASE
+        default: return nullptr;
+    }
+}
+
+int resident_grid(KernelFn fn, int lanes) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, lanes, 0) != hipSuccess)
+        return 0;
+    if (per_cu < 1) per_cu = 1;
+    return cus * per_cu;
+}
+
+}  // namespace
+
+namespace farn {
+
+int launch(const Call &c, int variant, int grid_cap) {
+    const RowShape rs = row_shape(c.H);
+    const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
+    const bool quant = c.q != nullptr;
+    KernelFn fn = quant ? pick<true>(variant, c.R, vi) : pick<false>(variant, c.R, vi);
+    if (!fn) return 1;
+
+    Params k;
+    for (int r = 0; r < 8; ++r) k.p[r] = c.partials[r];
+    k.res = c.residual;
+    k.gamma = c.gamma;
+    k.res_out = c.residual_out;
+    k.out = c.out;
+    k.q = c.q;
+    k.scales = c.scales;
+    k.T = c.T;
+    k.nvec = (int)(c.H / 8);
+    k.ngroups = (int)(c.H / 128);
+    k.h = (double)c.H;
+    k.eps = c.eps;
+
+    int64_t grid;
+    if (variant == 1) {
+        grid = c.T;
+    } else {
+        grid = resident_grid(fn, rs.lanes);
+        if (grid <= 0) return 1;
+        if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+        if (grid > c.T) grid = c.T;
+    }
+    hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3((uint32_t)rs.lanes), 0,
+                       (hipStream_t)c.stream, k);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace farn
