@@ -122,6 +122,30 @@ def time_calls(sets, variant, steps, warmup, grid_cap=0):
     return start.elapsed_time(end) / steps, wall / steps
 
 
+def time_graph(sets, variant, calls, replays, grid_cap=0):
+    """Average ms per call with the launches captured in a HIP graph (the way a serving loop
+    issues decode steps), so host launch overhead is out of the measurement. One graph holds
+    `calls` back-to-back calls rotating over `sets`; it is replayed `replays` times."""
+    for b in sets:
+        b.call(variant, grid_cap)  # warm the code objects before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            sets[i % len(sets)].call(variant, grid_cap)
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (replays * calls)
+    del g
+    return ms
+
+
 def parity_gate(d, bufs, quant, emit_out, rows):
     import oracle
     from tests.parity import compare_bf16, compare_fp8, from_dev_bf16, within_tolerance
@@ -179,24 +203,34 @@ def recorded_traffic(workload):
 
 
 def secondary(dev, steps):
-    """Decode shapes (us/call, hot = one buffer set, cold = sets rotated over >= 1 GiB) and the
-    plain prefill call."""
+    """Decode shapes in us/call: eager (one Python call per launch, host-bound), and graph
+    replay, hot (one buffer set, cache-resident) and cold (sets rotated over >= 1 GiB, so
+    every call streams from HBM); plus the plain prefill call."""
     out = {}
     for name in ("decode_ds", "decode_fp8"):
         cfg, quant, emit = WORKLOADS[name]
         d = make_inputs(cfg)
         b = Bufs(d, dev, quant, emit)
         nb = nbytes(cfg, quant, emit)
-        hot, hot_wall = time_calls([b], F.VARIANT_AUTO, steps, 20)
+        eager, _ = time_calls([b], F.VARIANT_AUTO, steps, 20)
+        hot = time_graph([b], F.VARIANT_AUTO, 200, 10)
         k = max(1, -(-(1 << 30) // nb))
         sets = [b] + [b.clone(dev) for _ in range(k - 1)]
-        cold, _ = time_calls(sets, F.VARIANT_AUTO, max(steps, 2 * k), 2 * k)
-        out[name] = {"us_per_call_hot": round(hot * 1e3, 2), "us_per_call_cold": round(cold * 1e3, 2),
-                     "us_per_call_wall_hot": round(hot_wall * 1e3, 2),
-                     "GBps_cold": round(nb / (cold * 1e-3) / 1e9, 1), "rotation_sets": k,
+        calls = k * max(1, 200 // k)
+        cold = time_graph(sets, F.VARIANT_AUTO, calls, max(2, 2000 // calls))
+        out[name] = {"us_per_call_graph_hot": round(hot * 1e3, 2),
+                     "us_per_call_graph_cold": round(cold * 1e3, 2),
+                     "us_per_call_eager": round(eager * 1e3, 2),
+                     "GBps_graph_cold": round(nb / (cold * 1e-3) / 1e9, 1), "rotation_sets": k,
                      "bytes_per_call": nb}
         del sets, b
         torch.cuda.empty_cache()
+    cfg, quant, emit = WORKLOADS["prefill"]
+    b = Bufs(make_inputs(cfg), dev, quant, emit)
+    ms, _ = time_calls([b], F.VARIANT_AUTO, 50, 5)
+    out["prefill"] = {"us_per_call": round(ms * 1e3, 2),
+                      "GBps": round(cfg.nbytes_plain / (ms * 1e-3) / 1e9, 1),
+                      "bytes_per_call": cfg.nbytes_plain}
     return out
 
 

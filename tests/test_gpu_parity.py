@@ -288,3 +288,38 @@ def test_nan_row(dev):
                                compare_bf16("out", from_dev_bf16(out)[[0, 1, 3]], ref[1]),
                                compare_fp8(qq[[0, 1, 3]], ref[2], s.cpu().numpy()[[0, 1, 3]], ref[3]))
     assert ok, why
+
+
+# ------------------------------------------------------------------ graph capture
+def test_graph_capture_replays_match_eager(dev):
+    """The calls allocate nothing and never synchronise, so a serving loop can capture them in a
+    HIP graph. Replay several times with the program's own eager work and synchronisations
+    between the replays; every replay must equal the eager result bit for bit."""
+    say("[gpu] graph capture")
+    ua = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=70), dev)
+    ub = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=71), dev)
+    ea = F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS)
+    eb = F.reduce_add_rmsnorm_quant_group(ub.P, ub.res, ub.g, EPS)
+    torch.cuda.synchronize()
+    ga = (torch.empty_like(ea[0]), torch.empty_like(ea[1]))
+    gb = tuple(torch.empty_like(x) for x in eb)
+    # warm up on a side stream, as graph capture requires
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS, residual_out=ga[0], out=ga[1])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS, residual_out=ga[0], out=ga[1])
+        F.reduce_add_rmsnorm_quant_group(ub.P, ub.res, ub.g, EPS, residual_out=gb[0], out=gb[1],
+                                         q=gb[2], scales=gb[3])
+    for rep in range(4):
+        for t in ga + gb:
+            t.view(torch.uint8).fill_(0xA5)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(ea + eb, ga + gb):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}"

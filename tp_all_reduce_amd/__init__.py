@@ -37,11 +37,11 @@ class FarnError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib.farn_status_string(status).decode()})")
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m tp_all_reduce_amd.build` "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m tp_all_reduce_amd.build` "
                           "(hipcc, gfx950). There is no fallback path.")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     pp = ctypes.POINTER(ctypes.c_void_p)
     base = [pp, i32, vp, vp, f32, i64, i64]
