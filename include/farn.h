@@ -105,8 +105,9 @@ farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int
                                                 float *scales, void *stream);
 
 /* Kernel variants. AUTO picks by size (farn_select_variant). LATENCY: one workgroup
-   per token row. BANDWIDTH: persistent workgroups that stream many rows each. Both
-   compute bit-identical results. */
+   per token row (grid = T). BANDWIDTH: persistent workgroups (grid = resident
+   workgroups) that stream many rows each, prefetching the next row. Both reduce each
+   row in the same order and compute bit-identical results. */
 typedef enum farn_variant {
     FARN_VARIANT_AUTO = 0,
     FARN_VARIANT_LATENCY = 1,

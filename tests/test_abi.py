@@ -53,10 +53,11 @@ def test_status_strings_and_select():
     for s in range(8):
         assert L.farn_status_string(s)
     assert L.farn_status_string(99) == b"unknown status"
-    for T in (1, 2, 64, 512):
-        assert F.select_variant(8, T, 7168, False) == F.VARIANT_LATENCY
-    for T in (4096, 8192, 1 << 20):
-        assert F.select_variant(8, T, 7168, True) == F.VARIANT_BANDWIDTH
+    for T in (1, 2, 64, 512, 4096, 8192, 1 << 20):
+        for H in (256, 7168, 8192):
+            assert F.select_variant(8, T, H, False) in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH)
+    assert F.select_variant(8, 64, 7168, False) == F.VARIANT_LATENCY  # decode
+    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_LATENCY  # prefill (measured best)
 
 
 class FakeCall:
