@@ -55,6 +55,11 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_bf16_from_double_array.restype = None
     L.oracle_e4m3fn_from_double_array.argtypes = [dp, ctypes.POINTER(ctypes.c_uint8), ctypes.c_int64]
     L.oracle_e4m3fn_from_double_array.restype = None
+    L.oracle_reduce.argtypes = [ctypes.POINTER(u16p), ctypes.c_int, ctypes.c_int64, ctypes.c_int64, u16p]
+    L.oracle_reduce.restype = ctypes.c_int
+    L.oracle_quant_group.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
+    L.oracle_quant_group.restype = ctypes.c_int
     return L
 
 
@@ -164,3 +169,26 @@ def e4m3fn_from_double_array(x) -> np.ndarray:
     lib().oracle_e4m3fn_from_double_array(x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
                                           y.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), x.size)
     return y
+
+
+def reduce(partials) -> np.ndarray:
+    """All-reduce alone: bf16 of the fp32 rank-order sum of the partials ([R,T,H] or list)."""
+    plist = _partials_list(partials)
+    T, H = plist[0].shape
+    out = np.empty((T, H), np.uint16)
+    if lib().oracle_reduce(_ptr_array(plist), len(plist), T, H, _u16(out)) != 0:
+        raise RuntimeError("oracle_reduce failed")
+    return out
+
+
+def quant_group(x, group: int = 128):
+    """Per-group E4M3 quant alone of a bf16 [T,H] array: returns (q uint8 [T,H], scales [T,H/group])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H), np.uint8)
+    scales = np.empty((T, H // group), np.float32)
+    rc = lib().oracle_quant_group(_u16(x), T, H, group, q.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                  scales.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    if rc != 0:
+        raise RuntimeError("oracle_quant_group failed")
+    return q, scales

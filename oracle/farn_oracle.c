@@ -263,3 +263,49 @@ void oracle_bf16_from_double_array(const double *x, uint16_t *y, int64_t n) {
 void oracle_e4m3fn_from_double_array(const double *x, uint8_t *y, int64_t n) {
     for (int64_t i = 0; i < n; ++i) y[i] = oracle_e4m3fn_from_double(x[i]);
 }
+
+/*
+ * Unfused building blocks, for the two- and three-kernel compositions the fused call
+ * replaces ("AMD fused AllReduce-RMSNorm quant kernel", sglang #24651 summary: the
+ * fallback chain runs AR + RMSNorm and then a separate per-1x128 quant, and the
+ * benchmark compares 3-, 2- and 1-kernel variants; "ROCm AITER fused all-reduce +
+ * RMSNorm", vLLM #37646 summary: the unfused pattern is tensor_model_parallel_all_reduce
+ * followed by rms_norm).
+ */
+
+/* All-reduce alone: out = bf16_rne(P_0 + P_1 + ... + P_{R-1}), fp32 left fold in rank order. */
+int oracle_reduce(const uint16_t *const *partials, int R, int64_t T, int64_t H, uint16_t *out) {
+    if (!partials || R < 1 || !out || T < 0 || H < 1) return -1;
+    for (int r = 0; r < R; ++r)
+        if (!partials[r]) return -1;
+    for (int64_t i = 0; i < T * H; ++i) {
+        float acc = bf16_to_float(partials[0][i]);
+        for (int r = 1; r < R; ++r) acc = acc + bf16_to_float(partials[r][i]);
+        out[i] = oracle_bf16_from_double((double)acc);
+    }
+    return 0;
+}
+
+/* Per-group quant alone, of a bf16 [T,H] input: step 6 of the header on x. */
+int oracle_quant_group(const uint16_t *x, int64_t T, int64_t H, int group, uint8_t *q,
+                       float *scales) {
+    if (!x || !q || !scales || T < 0 || H < 1 || group < 1 || H % group != 0) return -1;
+    const int64_t G = H / group;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t g = 0; g < G; ++g) {
+            const uint16_t *o = x + t * H + g * group;
+            double amax = 0.0;
+            for (int64_t h = 0; h < group; ++h) {
+                double v = fabs(bf16_to_double(o[h]));
+                if (v > amax || isnan(v)) amax = v;
+                if (isnan(amax)) break;
+            }
+            float scale = (float)(amax / 448.0);
+            scales[t * G + g] = scale;
+            for (int64_t h = 0; h < group; ++h)
+                q[t * H + g * group + h] =
+                    scale == 0.0f ? 0x00u : oracle_e4m3fn_from_double(bf16_to_double(o[h]) / (double)scale);
+        }
+    }
+    return 0;
+}

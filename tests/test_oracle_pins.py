@@ -360,6 +360,52 @@ def check_in_place_residual():
     assert np.array_equal(ro, ro2) and np.array_equal(out, out2)
 
 
+# ============================================================================ unfused blocks
+def check_reduce_alone():
+    """All-reduce alone: integer sums exact for every R; R=1 is the identity; the hand-built
+    fold-order row; against the bf16 nearest to the exact rational sum."""
+    rng = np.random.default_rng(5)
+    for R in range(1, 9):
+        P = rng.integers(-16, 17, size=(R, 3, 24))
+        assert np.array_equal(bf16_bits_to_float(oracle.reduce(f2b(P))), P.sum(axis=0).astype(np.float32))
+    d = make_inputs(CONFIGS["tiny"], seed=6, R=1, T=3, H=64)
+    assert np.array_equal(oracle.reduce(d["partials"]), d["partials"][0])
+    P = f2b(np.array([1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24])[:, None, None] * np.ones((1, 1, 8)))
+    assert np.all(oracle.reduce(P) == 0x3F80)
+    d = make_inputs(CONFIGS["tiny"], seed=7, R=8, T=3, H=32)
+    ar = oracle.reduce(d["partials"])
+    eq = 0
+    for t in range(3):
+        for h in range(32):
+            want = bf16_nearest(sum(bf16_bits_to_fraction(d["partials"][r, t, h]) for r in range(8)))
+            assert ulp_dist_bf16([want], [ar[t, h]])[0] <= 1
+            eq += int(want == ar[t, h])
+    assert eq >= 0.95 * 96
+
+
+def check_quant_alone():
+    """Quant alone on bf16 inputs with outliers: scale = IEEE single amax/448, a 448 code in every
+    nonzero group, codes = exact nearest E4M3 of the rational quotient, zero groups give zeros."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    x[:, rng.choice(512, 6, replace=False)] *= 20
+    x[2, 128:256] = 0.0
+    xb = f2b(x)
+    q, sc = oracle.quant_group(xb)
+    amax = np.abs(bf16_bits_to_float(xb)).reshape(4, 4, 128).max(axis=2).astype(np.float32)
+    assert np.array_equal(sc, amax / np.float32(448.0))
+    assert sc[2, 1] == 0 and np.all(q[2, 128:256] == 0)
+    qq = q.reshape(4, 4, 128) & 0x7F
+    assert np.all((qq == 0x7E).any(axis=2) | (amax == 0))
+    for t in range(4):
+        for h in range(0, 512, 3):
+            s = sc[t, h // 128]
+            if s == 0:
+                continue
+            v = bf16_bits_to_fraction(xb[t, h]) / Fraction(float(s))
+            assert q[t, h] == e4m3fn_nearest(v, negative_zero=(xb[t, h] == 0x8000)), (t, h)
+
+
 ALL_CHECKS = [
     check_bf16_encoder_vs_torch_cast, check_bf16_golden_rounding_points, check_bf16_encoder_exact_on_doubles,
     check_e4m3_encoder_exhaustive_bf16, check_e4m3_encoder_exact_near_ties, check_e4m3_golden_codes,
@@ -369,6 +415,7 @@ ALL_CHECKS = [
     check_scale_invariance,
     check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_dequant_bound,
     check_quant_zero_group_and_consistency, check_in_place_residual,
+    check_reduce_alone, check_quant_alone,
 ]
 
 
@@ -413,6 +460,11 @@ MUTANTS = [
     ("scale_transposed", "j->scales[t * G + g] = scale;", "j->scales[g * j->T + t] = scale;"),
     ("abs_dropped", "double v = fabs(bf16_to_double(o[h]));", "double v = bf16_to_double(o[h]);"),
     ("stats_on_gamma_scaled", "ss += y * y;", "ss += y * y * bf16_to_double(j->gamma[h]);"),
+    ("reduce_alone_drops_rank_1", "for (int r = 1; r < R; ++r) acc = acc + bf16_to_float(partials[r][i]);",
+     "for (int r = 2; r < R; ++r) acc = acc + bf16_to_float(partials[r][i]);"),
+    ("quant_alone_scale_240", "float scale = (float)(amax / 448.0);\n            scales[t * G + g] = scale;",
+     "float scale = (float)(amax / 240.0);\n            scales[t * G + g] = scale;"),
+    ("quant_alone_wrong_group_base", "const uint16_t *o = x + t * H + g * group;", "const uint16_t *o = x + t * H;"),
 ]
 
 
