@@ -91,6 +91,21 @@ class Bufs:
         c.alloc_outputs(dev)
         return c
 
+    def call_2kernel(self, variant=0, grid_cap=0):
+        """Fused AR + RMSNorm, then the quant alone (the pages' two-kernel fallback)."""
+        F.reduce_add_rmsnorm(self.P, self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
+                             variant=variant, grid_cap=grid_cap)
+        F.quant_group(self.out, q=self.q, scales=self.s)
+
+    def call_3kernel(self, variant=0, grid_cap=0):
+        """All-reduce alone, add + RMSNorm, then the quant alone (three kernels)."""
+        if not hasattr(self, "ar"):
+            self.ar = torch.empty_like(self.ro)
+        F.reduce(self.P, out=self.ar)
+        F.reduce_add_rmsnorm([self.ar], self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
+                             variant=variant, grid_cap=grid_cap)
+        F.quant_group(self.out, q=self.q, scales=self.s)
+
     def call(self, variant, grid_cap=0):
         if self.quant:
             F.reduce_add_rmsnorm_quant_group(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
@@ -105,34 +120,34 @@ def nbytes(cfg, quant, emit_out):
     return cfg.nbytes_quant(emit_out) if quant else cfg.nbytes_plain
 
 
-def time_calls(sets, variant, steps, warmup, grid_cap=0):
+def time_calls(sets, variant, steps, warmup, grid_cap=0, method="call"):
     """Average ms per call over `steps` back-to-back calls, rotating over `sets`, timed with
     events on the stream the kernels are launched on (torch's current stream)."""
     for i in range(warmup):
-        sets[i % len(sets)].call(variant, grid_cap)
+        getattr(sets[i % len(sets)], method)(variant, grid_cap)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
-        sets[i % len(sets)].call(variant, grid_cap)
+        getattr(sets[i % len(sets)], method)(variant, grid_cap)
     end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     return start.elapsed_time(end) / steps, wall / steps
 
 
-def time_graph(sets, variant, calls, replays, grid_cap=0):
+def time_graph(sets, variant, calls, replays, grid_cap=0, method="call"):
     """Average ms per call with the launches captured in a HIP graph (the way a serving loop
     issues decode steps), so host launch overhead is out of the measurement. One graph holds
     `calls` back-to-back calls rotating over `sets`; it is replayed `replays` times."""
     for b in sets:
-        b.call(variant, grid_cap)  # warm the code objects before capture
+        getattr(b, method)(variant, grid_cap)  # warm the code objects before capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(calls):
-            sets[i % len(sets)].call(variant, grid_cap)
+            getattr(sets[i % len(sets)], method)(variant, grid_cap)
     g.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -234,6 +249,29 @@ def secondary(dev, steps):
     return out
 
 
+def unfused(dev):
+    """What fusion buys: the FP8 step as one kernel (fused), two (fused AR+RMSNorm, then quant)
+    and three (all-reduce, add+RMSNorm, quant), as the sglang benchmark compares them. Prefill:
+    eager, streaming from HBM. Decode: graph replay, cache-hot."""
+    res = {}
+    for name in ("prefill_fp8", "decode_fp8", "decode_ds"):
+        cfg = WORKLOADS[name][0]
+        b = Bufs(make_inputs(cfg), dev, True, True)
+        rec = {}
+        for method, label in (("call", "1_kernel"), ("call_2kernel", "2_kernel"), ("call_3kernel", "3_kernel")):
+            if name.startswith("prefill"):
+                ms, _ = time_calls([b], F.VARIANT_AUTO, 30, 3, method=method)
+            else:
+                ms = time_graph([b], F.VARIANT_AUTO, 100, 10, method=method)
+            rec[label + "_us"] = round(ms * 1e3, 2)
+        rec["speedup_vs_3_kernel"] = round(rec["3_kernel_us"] / rec["1_kernel_us"], 2)
+        rec["speedup_vs_2_kernel"] = round(rec["2_kernel_us"] / rec["1_kernel_us"], 2)
+        res[name] = rec
+        del b
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +356,8 @@ def main():
         torch.cuda.empty_cache()
         log("secondary decode shapes")
         result["secondary"] = secondary(dev, 200)
+        log("unfused compositions")
+        result["secondary"]["unfused_fp8"] = unfused(dev)
     print(json.dumps(result), flush=True)
 
 

@@ -127,6 +127,30 @@ farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, 
                                                    float *scales, void *stream, int variant,
                                                    int grid_cap);
 
+/*
+ * Unfused building blocks: the kernels the fused calls replace. The sglang #24651
+ * summary ("AMD fused AllReduce-RMSNorm quant kernel", layernorm.py snippet and
+ * benchmark file list) falls back from the one-kernel AR + RMSNorm + quant to AR +
+ * RMSNorm followed by a separate per-1x128 quant, and benchmarks 3-, 2- and 1-kernel
+ * variants; the vLLM #37646 summary's unfused pattern is all-reduce then rms_norm.
+ * With these, the 2-kernel path is farn_reduce_add_rmsnorm + farn_quant_group and the
+ * 3-kernel path is farn_reduce + farn_reduce_add_rmsnorm (R = 1, the all-reduce output
+ * as its one partial) + farn_quant_group. Results follow each block's own definition,
+ * so the 3-kernel path rounds the all-reduce output to bf16 before the residual add.
+ */
+
+/* All-reduce alone: out[t,h] = bf16_rne(P_0 + ... + P_{R-1}), fp32 adds in rank order.
+ *   partials  host array of R device pointers, bf16 [T,H]; out device bf16 [T,H] (may not
+ *   overlap a partial). Same checks and status codes as the fused calls. */
+farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H, void *out,
+                        void *stream);
+
+/* Per-group quant alone of a bf16 [T,H] input x: scales[t,g] = amax/448 over channels
+ * [128g, 128g+128) of row t, q = E4M3 codes of x/scale (one rounding, satfinite, 0 for a
+ * zero group). group_size must be 128; H % 128 == 0; q and scales may not overlap x. */
+farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
+                             float *scales, void *stream);
+
 /* The variant AUTO would run for this shape (no validation; pure function of its arguments). */
 int farn_select_variant(int R, int64_t T, int64_t H, int quant);
 

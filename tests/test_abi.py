@@ -162,3 +162,44 @@ def test_validation_unit_is_hip_free():
     text = open(src).read()
     assert "hip/" not in text and "hip" not in re.findall(r"#include\s*[<\"]([^>\"]+)", text)
     subprocess.run(["g++", "-std=c++17", "-fsyntax-only", "-Wall", "-Wextra", "-Werror", src], check=True)
+
+
+def reduce_call(partials=(0x10_0000_0000, 0x10_1000_0000), R=None, T=4, H=256, out=0x10_2000_0000):
+    R = len(partials) if R is None else R
+    arr = (ctypes.c_void_p * max(1, len(partials)))(*partials) if partials is not None else None
+    return L.farn_reduce(arr, R, T, H, out, None)
+
+
+def quant_call(x=0x10_0000_0000, T=4, H=256, group=128, q=0x10_1000_0000, scales=0x10_2000_0000):
+    return L.farn_quant_group(x, T, H, group, q, scales, None)
+
+
+UNFUSED_REJECTIONS = [
+    ("reduce partials NULL", lambda: reduce_call(partials=None, R=2), NULL),
+    ("reduce a partial NULL", lambda: reduce_call(partials=(0x10_0000_0000, 0)), NULL),
+    ("reduce out NULL", lambda: reduce_call(out=0), NULL),
+    ("reduce R = 9", lambda: reduce_call(R=9), SHAPE),
+    ("reduce H % 8", lambda: reduce_call(H=12), SHAPE),
+    ("reduce T < 0", lambda: reduce_call(T=-2), SHAPE),
+    ("reduce misaligned out", lambda: reduce_call(out=0x10_2000_0008), ALIGN),
+    ("reduce out overlaps a partial", lambda: reduce_call(out=0x10_1000_0000 + 512), ALIAS),
+    ("quant x NULL", lambda: quant_call(x=0), NULL),
+    ("quant q NULL", lambda: quant_call(q=0), NULL),
+    ("quant scales NULL", lambda: quant_call(scales=0), NULL),
+    ("quant group 64", lambda: quant_call(group=64), SHAPE),
+    ("quant H % 128", lambda: quant_call(H=200), SHAPE),
+    ("quant misaligned q", lambda: quant_call(q=0x10_1000_0004), ALIGN),
+    ("quant misaligned scales", lambda: quant_call(scales=0x10_2000_0002), ALIGN),
+    ("quant q overlaps x", lambda: quant_call(q=0x10_0000_0000 + 64), ALIAS),
+    ("quant scales overlap q", lambda: quant_call(scales=0x10_1000_0000 + 64), ALIAS),
+]
+
+
+@pytest.mark.parametrize("what,fn,want", UNFUSED_REJECTIONS, ids=[r[0] for r in UNFUSED_REJECTIONS])
+def test_unfused_rejections(what, fn, want):
+    assert fn() == want, what
+
+
+def test_unfused_empty():
+    assert reduce_call(T=0, out=0) == OK
+    assert quant_call(T=0, x=0, q=0, scales=0) == OK

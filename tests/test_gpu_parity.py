@@ -323,3 +323,58 @@ def test_graph_capture_replays_match_eager(dev):
         torch.cuda.synchronize()
         for x, y in zip(ea + eb, ga + gb):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}"
+
+
+# ------------------------------------------------------------------ unfused building blocks
+@pytest.mark.parametrize("name", ["decode_ds", "decode_fp8", "tiny"])
+def test_unfused_blocks_and_compositions(dev, name):
+    """The all-reduce alone and the quant alone match their oracle blocks bit for bit; the
+    2-kernel composition (fused AR+RMSNorm, then quant) equals the fused FP8 call; the 3-kernel
+    composition (AR, then add+RMSNorm with the AR output as one partial, then quant) matches the
+    oracle's composition of the same blocks."""
+    cfg = CONFIGS[name]
+    d = make_inputs(cfg, seed=80)
+    u = Uploaded(d, dev)
+    say(f"[gpu] unfused blocks {name}")
+    ar = F.reduce(u.P)
+    torch.cuda.synchronize()
+    ref_ar = oracle.reduce(d["partials"])
+    assert np.array_equal(from_dev_bf16(ar), ref_ar)
+    if cfg.H % 128:
+        return
+    # 2-kernel: fused plain call, then quant alone
+    ro2, out2 = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS)
+    q2, s2 = F.quant_group(out2)
+    fused = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS)
+    torch.cuda.synchronize()
+    for x, y in zip((ro2, out2, q2, s2), fused):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    rq, rs = oracle.quant_group(from_dev_bf16(out2))
+    ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro2), from_dev_bf16(ro2)), None,
+                               compare_fp8(q2.cpu().numpy(), rq, s2.cpu().numpy(), rs))
+    assert ok and np.array_equal(q2.cpu().numpy(), rq), why
+    # 3-kernel: AR alone, add + RMSNorm on it, quant alone
+    ro3, out3 = F.reduce_add_rmsnorm([ar], u.res, u.g, EPS)
+    q3, s3 = F.quant_group(out3)
+    torch.cuda.synchronize()
+    r_ro3, r_out3 = oracle.reduce_add_rmsnorm(ref_ar[None], d["residual"], d["gamma"], EPS)
+    r_q3, r_s3 = oracle.quant_group(r_out3)
+    ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro3), r_ro3),
+                               compare_bf16("out", from_dev_bf16(out3), r_out3),
+                               compare_fp8(q3.cpu().numpy(), r_q3, s3.cpu().numpy(), r_s3))
+    assert ok, why
+
+
+@pytest.mark.parametrize("H", [128, 4096, 7168, 16384, 32768])
+def test_quant_alone_shapes(dev, H):
+    rng = np.random.default_rng(H)
+    x = rng.standard_normal((5, H)).astype(np.float32)
+    x[:, rng.choice(H, max(1, H // 100), replace=False)] *= 20
+    x[3, :128] = 0
+    import torch as _t
+    xb = _t.from_numpy(x).to(_t.bfloat16).view(_t.int16).numpy().view(np.uint16)
+    say(f"[gpu] quant alone H={H}")
+    q, s = F.quant_group(to_dev_bf16(xb, dev))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_group(xb)
+    assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)

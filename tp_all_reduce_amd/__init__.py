@@ -28,6 +28,7 @@ VARIANT_AUTO, VARIANT_LATENCY, VARIANT_BANDWIDTH = 0, 1, 2
 MAX_R, MAX_H, GROUP = 8, 32768, 128
 EXPORTS = ("farn_reduce_add_rmsnorm", "farn_reduce_add_rmsnorm_quant_group",
            "farn_reduce_add_rmsnorm_ex", "farn_reduce_add_rmsnorm_quant_group_ex",
+           "farn_reduce", "farn_quant_group",
            "farn_select_variant", "farn_status_string", "farn_abi_version")
 
 
@@ -39,7 +40,7 @@ class FarnError(RuntimeError):
 
 def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
-        raise ImportError(f"{path} is not built; run `python -m tp_all_reduce_amd.build` "
+        raise ImportError(f"{path} is not built; run `python tp_all_reduce_amd/build.py` "
                           "(hipcc, gfx950). There is no fallback path.")
     L = ctypes.CDLL(path)
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
@@ -49,7 +50,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.farn_reduce_add_rmsnorm_quant_group.argtypes = base + [i32, vp, vp, vp, vp, vp]
     L.farn_reduce_add_rmsnorm_ex.argtypes = base + [vp, vp, vp, i32, i32]
     L.farn_reduce_add_rmsnorm_quant_group_ex.argtypes = base + [i32, vp, vp, vp, vp, vp, i32, i32]
-    for fn in EXPORTS[:4]:
+    L.farn_reduce.argtypes = [pp, i32, i64, i64, vp, vp]
+    L.farn_quant_group.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    for fn in EXPORTS[:6]:
         getattr(L, fn).restype = i32
     L.farn_select_variant.argtypes = [i32, i64, i64, i32]
     L.farn_select_variant.restype = i32
@@ -155,3 +158,33 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
     return residual_out, out, q, scales
+
+
+def reduce(partials, *, out=None, stream=None):
+    """All-reduce alone (first kernel of the unfused compositions): bf16 of the fp32 rank-order
+    sum of the partials. Returns out."""
+    p0 = partials[0]
+    T, H = p0.shape
+    dev = p0.device
+    for i, p in enumerate(partials):
+        _check_bf16(f"partials[{i}]", p, (T, H), dev)
+    out = torch.empty_like(p0) if out is None else out
+    _check_bf16("out", out, (T, H), dev)
+    st = _lib.farn_reduce(_ptr_array(partials), len(partials), T, H, _ptr(out), _stream(dev, stream))
+    if st != OK:
+        raise FarnError(st, "farn_reduce")
+    return out
+
+
+def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None):
+    """Per-group E4M3 quant alone of a bf16 [T,H] tensor. Returns (q uint8 [T,H], scales fp32 [T,H/128])."""
+    T, H = x.shape
+    dev = x.device
+    _check_bf16("x", x, (T, H), dev)
+    q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
+    G = H // group_size if group_size > 0 else 0
+    scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
+    st = _lib.farn_quant_group(_ptr(x), T, H, group_size, _ptr(q), _ptr(scales), _stream(dev, stream))
+    if st != OK:
+        raise FarnError(st, "farn_quant_group")
+    return q, scales

@@ -1,6 +1,8 @@
 """Build libfarn.so (gfx950) in-tree with hipcc.
 
-    python -m tp_all_reduce_amd.build
+    python tp_all_reduce_amd/build.py
+
+(Run it by path: importing the package loads the built library.)
 
 The C-ABI layer (csrc/farn_api.cpp) makes no HIP call and is compiled by g++; the
 kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two.

@@ -137,9 +137,90 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     return farn::launch(c, variant, grid_cap) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
+// Checks of the standalone all-reduce: partials -> out.
+farn_status check_reduce(const void *const *partials, int R, int64_t T, int64_t H, void *out) {
+    if (R < 1 || R > FARN_MAX_R) return FARN_ERR_SHAPE;
+    if (T < 0 || T > ((int64_t)1 << 40) || H <= 0 || H % 8 != 0 || H > FARN_MAX_H) return FARN_ERR_SHAPE;
+    if (!partials) return FARN_ERR_NULL;
+    if (T == 0) return FARN_OK;
+    for (int r = 0; r < R; ++r)
+        if (!partials[r]) return FARN_ERR_NULL;
+    if (!out) return FARN_ERR_NULL;
+    auto a16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+    for (int r = 0; r < R; ++r)
+        if (!a16(partials[r])) return FARN_ERR_ALIGN;
+    if (!a16(out)) return FARN_ERR_ALIGN;
+    const Range o = range_of(out, T * H * 2);
+    for (int r = 0; r < R; ++r)
+        if (overlaps(o, range_of(partials[r], T * H * 2))) return FARN_ERR_ALIAS;
+    return FARN_OK;
+}
+
+// Checks of the standalone quant: x -> (q, scales).
+farn_status check_quant(const void *x, int64_t T, int64_t H, int group_size, void *q, float *scales) {
+    if (T < 0 || T > ((int64_t)1 << 40) || H <= 0 || H > FARN_MAX_H || group_size != FARN_GROUP ||
+        H % FARN_GROUP != 0)
+        return FARN_ERR_SHAPE;
+    if (T == 0) return FARN_OK;
+    if (!x || !q || !scales) return FARN_ERR_NULL;
+    if (((uintptr_t)x & 15u) || ((uintptr_t)q & 15u) || ((uintptr_t)scales & 3u)) return FARN_ERR_ALIGN;
+    const Range rx = range_of(x, T * H * 2), rq = range_of(q, T * H),
+                rs = range_of(scales, T * (H / FARN_GROUP) * 4);
+    if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return FARN_ERR_ALIAS;
+    return FARN_OK;
+}
+
+farn::Call blank_call(void *stream) {
+    farn::Call c;
+    for (int r = 0; r < 8; ++r) c.partials[r] = nullptr;
+    c.R = 0;
+    c.residual = nullptr;
+    c.gamma = nullptr;
+    c.eps = 0.0f;
+    c.T = 0;
+    c.H = 0;
+    c.residual_out = nullptr;
+    c.out = nullptr;
+    c.q = nullptr;
+    c.scales = nullptr;
+    c.x = nullptr;
+    c.stream = stream;
+    return c;
+}
+
 }  // namespace
 
 extern "C" {
+
+farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H, void *out,
+                        void *stream) {
+    farn_status st = check_reduce(partials, R, T, H, out);
+    if (st != FARN_OK || T == 0) return st;
+    if (T > INT32_MAX) return FARN_ERR_SHAPE;
+    farn::Call c = blank_call(stream);
+    c.kind = farn::Kind::kReduce;
+    for (int r = 0; r < R; ++r) c.partials[r] = partials[r];
+    c.R = R;
+    c.T = T;
+    c.H = H;
+    c.residual_out = out;
+    return farn::launch(c, FARN_VARIANT_LATENCY, 0) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+}
+
+farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
+                             float *scales, void *stream) {
+    farn_status st = check_quant(x, T, H, group_size, q, scales);
+    if (st != FARN_OK || T == 0) return st;
+    if (T > INT32_MAX) return FARN_ERR_SHAPE;
+    farn::Call c = blank_call(stream);
+    c.kind = farn::Kind::kQuant;
+    c.T = T;
+    c.H = H;
+    c.x = x;
+    c.q = q;
+    c.scales = scales;
+    return farn::launch(c, FARN_VARIANT_LATENCY, 0) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+}
 
 farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,
                                     const void *gamma, float eps, int64_t T, int64_t H,

@@ -6,8 +6,12 @@
 
 namespace farn {
 
+enum class Kind { kFused, kReduce, kQuant };
+
 // One validated call, raw device pointers. q / scales are null for the plain call.
+// kReduce writes the all-reduce alone into residual_out; kQuant reads x.
 struct Call {
+    Kind kind = Kind::kFused;
     const void *partials[8];
     int R;
     const void *residual;  // null: no residual
@@ -18,6 +22,7 @@ struct Call {
     void *out;     // null only for the quant call with the bf16 output off
     void *q;       // quant call only
     float *scales; // quant call only
+    const void *x = nullptr;  // kQuant input
     void *stream;
 };
 

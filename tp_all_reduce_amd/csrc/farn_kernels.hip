@@ -52,6 +52,7 @@ struct Params {
     void *out;          // null: bf16 output not written (quant call only)
     void *q;            // E4M3 codes [T,H] (quant only)
     float *scales;      // [T, H/128] (quant only)
+    const void *x;      // bf16 [T,H] input of the standalone quant kernel
     int64_t T;
     int nvec;           // H / 8
     int ngroups;        // H / 128
@@ -229,9 +230,7 @@ __device__ __forceinline__ void load_slot(SlotIn<R> &in, const Params &k, int64_
 // is none), rounded to bf16 and stored as residual_out; accumulates the squares of the
 // rounded values into ss (fp64). Lanes past the row end see zeros and add nothing.
 template <int R>
-__device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
-                                             uint32_t off, double &ss) {
-    const bool has_res = k.res != nullptr;
+__device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
     u32x4 packed;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -246,6 +245,13 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
         const float hi_r = hi + bf_hi(in.res[w]);
         packed[w] = pack_bf16(has_res ? lo_r : lo, has_res ? hi_r : hi);
     }
+    return packed;
+}
+
+template <int R>
+__device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
+                                             uint32_t off, double &ss) {
+    const u32x4 packed = fold_slot<R>(in, k.res != nullptr);
     st16(packed, ro_out, off);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -277,6 +283,30 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     return 1.0 / __builtin_sqrt(tot / (double)k.h + (double)k.eps);
 }
 
+// E4M3 codes of one vector slot (8 bf16 values as floats) and, from one lane per
+// 16-lane group, the group's scale.
+__device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
+    amax = row16_umax(amax);  // 16 lanes = one 128-channel group
+    const float scale = __uint_as_float(amax) / 448.0f;  // correctly rounded
+    // An all-zero group has scale 0 and all codes 0: inv = 0 keeps every lane on the
+    // arithmetic path (no per-element branch) and the mask clears the codes.
+    const float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
+    const uint32_t keep = scale == 0.0f ? 0u : 0xffu;
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = e4m3_code(o[e], scale, inv) & keep;
+    u32x2 codes;
+    codes[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    st8(codes, r_q, off >> 1);
+    // one lane per group writes the scale; the others aim past the row (dropped)
+    const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? (off >> 8) * 4u : kDropOffset;
+    st4(scale, r_sc, soff);
+}
+
 // Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16), store
 // out, and (QUANT) its E4M3 codes and group scale.
 template <bool QUANT>
@@ -293,27 +323,7 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
         o[2 * w + 1] = bf_hi(packed[w]);
     }
     st16(packed, r_out, off);
-    if constexpr (QUANT) {
-        uint32_t amax = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
-        amax = row16_umax(amax);  // 16 lanes = one 128-channel group
-        const float scale = __uint_as_float(amax) / 448.0f;  // correctly rounded
-        // An all-zero group has scale 0 and all codes 0: inv = 0 keeps every lane on the
-        // arithmetic path (no per-element branch) and the mask clears the codes.
-        const float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
-        const uint32_t keep = scale == 0.0f ? 0u : 0xffu;
-        uint32_t c[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = e4m3_code(o[e], scale, inv) & keep;
-        u32x2 codes;
-        codes[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-        codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        st8(codes, r_q, off >> 1);
-        // one lane per group writes the scale; the others aim past the row (dropped)
-        const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? (off >> 8) * 4u : kDropOffset;
-        st4(scale, r_sc, soff);
-    }
+    if constexpr (QUANT) quant_slot(o, r_q, r_sc, off);
 }
 
 // Whole row t with the loads of slot 0 already issued into `in0` (VPL > 1 loads and
@@ -389,6 +399,45 @@ __global__ __launch_bounds__(1024) void farn_bandwidth(const Params k) {
     }
 }
 
+// Unfused building blocks (the compositions the fused call replaces): the all-reduce
+// alone, and the per-group quant alone of a bf16 tensor. Same row mapping, loads and
+// arithmetic as the fused kernel's corresponding steps.
+template <int R, int VPL>
+__global__ __launch_bounds__(1024) void farn_reduce_rows(const Params k) {
+    const int64_t t = blockIdx.x;
+    const int rb = k.nvec * 16;
+    const rsrc_t r_out = row_rsrc(k.res_out, t * (int64_t)rb, rb);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        const uint32_t off = (v * blockDim.x + threadIdx.x) * 16u;
+        SlotIn<R> in;
+        load_slot<R>(in, k, t, off);
+        st16(fold_slot<R>(in, false), r_out, off);
+    }
+}
+
+template <int VPL>
+__global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
+    const int64_t t = blockIdx.x;
+    const int rb = k.nvec * 16;
+    const rsrc_t r_x = row_rsrc(k.x, t * (int64_t)rb, rb);
+    const rsrc_t r_q = row_rsrc(k.q, t * (int64_t)k.nvec * 8, k.nvec * 8);
+    const rsrc_t r_sc = row_rsrc(k.scales, t * (int64_t)k.ngroups * 4, k.ngroups * 4);
+    u32x4 xv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) xv[v] = ld16(r_x, (v * blockDim.x + threadIdx.x) * 16u);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+        float o[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            o[2 * w] = bf_lo(xv[v][w]);
+            o[2 * w + 1] = bf_hi(xv[v][w]);
+        }
+        quant_slot(o, r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u);
+    }
+}
+
 // ---------------------------------------------------------------- dispatch tables
 typedef void (*KernelFn)(const Params);
 
@@ -399,6 +448,24 @@ struct Row {
     static constexpr KernelFn bw[3] = {farn_bandwidth<R, 1, Q>, farn_bandwidth<R, 2, Q>,
                                        farn_bandwidth<R, 4, Q>};
 };
+
+template <int R>
+struct RedRow {
+    static constexpr KernelFn fn[3] = {farn_reduce_rows<R, 1>, farn_reduce_rows<R, 2>,
+                                       farn_reduce_rows<R, 4>};
+};
+constexpr KernelFn kQuantRows[3] = {farn_quant_rows<1>, farn_quant_rows<2>, farn_quant_rows<4>};
+
+KernelFn pick_reduce(int R, int vi) {
+    switch (R) {
+#define FARN_CASE(n) \
+    case n: return RedRow<n>::fn[vi];
+        FARN_CASE(1) FARN_CASE(2) FARN_CASE(3) FARN_CASE(4)
+        FARN_CASE(5) FARN_CASE(6) FARN_CASE(7) FARN_CASE(8)
+#undef FARN_CASE
+        default: return nullptr;
+    }
+}
 
 template <bool Q>
 KernelFn pick(int variant, int R, int vi) {
@@ -429,8 +496,17 @@ namespace farn {
 int launch(const Call &c, int variant, int grid_cap) {
     const RowShape rs = row_shape(c.H);
     const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
-    const bool quant = c.q != nullptr;
-    KernelFn fn = quant ? pick<true>(variant, c.R, vi) : pick<false>(variant, c.R, vi);
+    KernelFn fn = nullptr;
+    if (c.kind == Kind::kReduce) {
+        fn = pick_reduce(c.R, vi);
+        variant = 1;
+    } else if (c.kind == Kind::kQuant) {
+        fn = kQuantRows[vi];
+        variant = 1;
+    } else {
+        const bool quant = c.q != nullptr;
+        fn = quant ? pick<true>(variant, c.R, vi) : pick<false>(variant, c.R, vi);
+    }
     if (!fn) return 1;
 
     Params k;
@@ -441,6 +517,7 @@ int launch(const Call &c, int variant, int grid_cap) {
     k.out = c.out;
     k.q = c.q;
     k.scales = c.scales;
+    k.x = c.x;
     k.T = c.T;
     k.nvec = (int)(c.H / 8);
     k.ngroups = (int)(c.H / 128);
