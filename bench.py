@@ -91,63 +91,63 @@ class Bufs:
         c.alloc_outputs(dev)
         return c
 
-    def call_2kernel(self, variant=0, grid_cap=0):
+    def call_2kernel(self, variant=0):
         """Fused AR + RMSNorm, then the quant alone (the pages' two-kernel fallback)."""
         F.reduce_add_rmsnorm(self.P, self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
-                             variant=variant, grid_cap=grid_cap)
+                             variant=variant)
         F.quant_group(self.out, q=self.q, scales=self.s)
 
-    def call_3kernel(self, variant=0, grid_cap=0):
+    def call_3kernel(self, variant=0):
         """All-reduce alone, add + RMSNorm, then the quant alone (three kernels)."""
         if not hasattr(self, "ar"):
             self.ar = torch.empty_like(self.ro)
         F.reduce(self.P, out=self.ar)
         F.reduce_add_rmsnorm([self.ar], self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
-                             variant=variant, grid_cap=grid_cap)
+                             variant=variant)
         F.quant_group(self.out, q=self.q, scales=self.s)
 
-    def call(self, variant, grid_cap=0):
+    def call(self, variant):
         if self.quant:
             F.reduce_add_rmsnorm_quant_group(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
                                              residual_out=self.ro, out=self.out, q=self.q, scales=self.s,
-                                             variant=variant, grid_cap=grid_cap)
+                                             variant=variant)
         else:
             F.reduce_add_rmsnorm(self.P, self.res, self.g, 1e-6, residual_out=self.ro, out=self.out,
-                                 variant=variant, grid_cap=grid_cap)
+                                 variant=variant)
 
 
 def nbytes(cfg, quant, emit_out):
     return cfg.nbytes_quant(emit_out) if quant else cfg.nbytes_plain
 
 
-def time_calls(sets, variant, steps, warmup, grid_cap=0, method="call"):
+def time_calls(sets, variant, steps, warmup, method="call"):
     """Average ms per call over `steps` back-to-back calls, rotating over `sets`, timed with
     events on the stream the kernels are launched on (torch's current stream)."""
     for i in range(warmup):
-        getattr(sets[i % len(sets)], method)(variant, grid_cap)
+        getattr(sets[i % len(sets)], method)(variant)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for i in range(steps):
-        getattr(sets[i % len(sets)], method)(variant, grid_cap)
+        getattr(sets[i % len(sets)], method)(variant)
     end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
     return start.elapsed_time(end) / steps, wall / steps
 
 
-def time_graph(sets, variant, calls, replays, grid_cap=0, method="call"):
+def time_graph(sets, variant, calls, replays, method="call"):
     """Average ms per call with the launches captured in a HIP graph (the way a serving loop
     issues decode steps), so host launch overhead is out of the measurement. One graph holds
     `calls` back-to-back calls rotating over `sets`; it is replayed `replays` times."""
     for b in sets:
-        getattr(b, method)(variant, grid_cap)  # warm the code objects before capture
+        getattr(b, method)(variant)  # warm the code objects before capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(calls):
-            getattr(sets[i % len(sets)], method)(variant, grid_cap)
+            getattr(sets[i % len(sets)], method)(variant)
     g.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -279,7 +279,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_fp8", choices=sorted(WORKLOADS))
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANT_NAMES))
-    ap.add_argument("--grid-cap", type=int, default=0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step back to back for this long before the warmup steps, so the "
+                         "GPU clocks reach their sustained state (the first ~100 calls run slower)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -305,7 +307,7 @@ def main():
 
     parity = None
     if not args.no_parity:
-        bufs.call(variant, args.grid_cap)
+        bufs.call(variant)
         torch.cuda.synchronize()
         rng = np.random.default_rng(1)
         rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 32)]))
@@ -324,8 +326,16 @@ def main():
         log("copy calibration: 1 GiB read + 1 GiB written")
         del src, dst
 
-    log(f"timing {args.steps} steps after {args.warmup} warmup")
-    ms, wall_ms = time_calls([bufs], variant, args.steps, args.warmup, args.grid_cap)
+    settle_calls = 0
+    if args.settle_ms > 0:
+        t_end = time.perf_counter() + args.settle_ms / 1e3
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                bufs.call(variant)
+            settle_calls += 10
+            torch.cuda.synchronize()
+    log(f"timing {args.steps} steps after {settle_calls} settle calls and {args.warmup} warmup")
+    ms, wall_ms = time_calls([bufs], variant, args.steps, args.warmup)
     gbps = nb / (ms * 1e-3) / 1e9
     ran = F.select_variant(cfg.R, cfg.T, cfg.H, quant) if variant == F.VARIANT_AUTO else variant
     traffic = recorded_traffic(args.workload)
@@ -339,11 +349,12 @@ def main():
                    "variant": {1: "latency", 2: "bandwidth"}[ran], "bytes_per_step": nb,
                    "seed": cfg.seed},
         "us_per_call": round(ms * 1e3, 2), "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
+        "settle_calls": settle_calls,
         "wall_us_per_call": round(wall_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
-                     "kernel": "farn_" + {1: "latency", 2: "bandwidth"}[ran],
+                     "kernel": "farn_rows (" + {1: "latency", 2: "bandwidth"}[ran] + " shape)",
                      "algorithmic_bytes_per_launch": nb,
                      "hbm_bytes_per_launch": traffic},
         "parity": parity,

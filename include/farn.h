@@ -62,7 +62,7 @@ typedef enum farn_status {
                              overlap: residual_out == residual exactly, in place) */
     FARN_ERR_EPS = 5,     /* eps is not finite or is negative */
     FARN_ERR_LAUNCH = 6,  /* the kernel launch failed */
-    FARN_ERR_VARIANT = 7  /* unknown variant or negative grid cap in an _ex call */
+    FARN_ERR_VARIANT = 7  /* unknown variant in an _ex call */
 } farn_status;
 
 /* Largest TP degree the pages run is 8 ("[AMD] Support --enable-aiter-allreduce-fusion
@@ -72,7 +72,7 @@ typedef enum farn_status {
 #define FARN_MAX_H 32768
 /* Quant group along H ("per-1x128", group_size=128 in the sglang #24651 summary). */
 #define FARN_GROUP 128
-#define FARN_ABI_VERSION 1
+#define FARN_ABI_VERSION 2
 
 /*
  * Plain call: reduce + residual add + RMSNorm.
@@ -104,28 +104,27 @@ farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int
                                                 void *residual_out, void *out, void *q,
                                                 float *scales, void *stream);
 
-/* Kernel variants. AUTO picks by size (farn_select_variant). LATENCY: one workgroup
-   per token row (grid = T). BANDWIDTH: persistent workgroups (grid = resident
-   workgroups) that stream many rows each, prefetching the next row. Both reduce each
-   row in the same order and compute bit-identical results. */
+/* Launch shapes of the one kernel (one workgroup per token row). AUTO picks by size
+   (farn_select_variant). LATENCY: the widest row mapping (up to 1024 lanes, one 16-byte
+   vector per lane up to H = 8192), the shortest per-row chain, for small T. BANDWIDTH:
+   about half as many lanes with two vectors each (4096 < H <= 8192), so several rows
+   share a CU, for large T. Both compute the same results (their fp64 sums of squares
+   differ only in the order of additions). */
 typedef enum farn_variant {
     FARN_VARIANT_AUTO = 0,
     FARN_VARIANT_LATENCY = 1,
     FARN_VARIANT_BANDWIDTH = 2
 } farn_variant;
 
-/* As the calls above, with the variant forced and, for BANDWIDTH, the number of
-   workgroups capped (grid_cap = 0: the library's choice). For tests and the bench. */
+/* As the calls above, with the launch shape forced. For tests and the bench. */
 farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
                                        const void *gamma, float eps, int64_t T, int64_t H,
-                                       void *residual_out, void *out, void *stream,
-                                       int variant, int grid_cap);
+                                       void *residual_out, void *out, void *stream, int variant);
 farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, int R,
                                                    const void *residual, const void *gamma,
                                                    float eps, int64_t T, int64_t H, int group_size,
                                                    void *residual_out, void *out, void *q,
-                                                   float *scales, void *stream, int variant,
-                                                   int grid_cap);
+                                                   float *scales, void *stream, int variant);
 
 /*
  * Unfused building blocks: the kernels the fused calls replace. The sglang #24651

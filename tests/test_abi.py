@@ -57,7 +57,9 @@ def test_status_strings_and_select():
         for H in (256, 7168, 8192):
             assert F.select_variant(8, T, H, False) in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH)
     assert F.select_variant(8, 64, 7168, False) == F.VARIANT_LATENCY  # decode
-    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_LATENCY  # prefill (measured best)
+    assert F.select_variant(8, 16, 4096, True) == F.VARIANT_LATENCY  # decode FP8
+    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_BANDWIDTH  # prefill (measured best)
+    assert F.select_variant(8, 8192, 8192, False) == F.VARIANT_LATENCY  # wide wins at H = 8192
 
 
 class FakeCall:
@@ -76,17 +78,15 @@ class FakeCall:
         self.eps = 1e-6
         self.group = 128
         self.variant = 0
-        self.grid_cap = 0
 
     def call(self):
         arr = (ctypes.c_void_p * max(1, len(self.partials)))(*self.partials) if self.partials is not None else None
         if self.quant:
             return L.farn_reduce_add_rmsnorm_quant_group_ex(
                 arr, self.R, self.residual, self.gamma, self.eps, self.T, self.H, self.group,
-                self.residual_out, self.out, self.q, self.scales, None, self.variant, self.grid_cap)
+                self.residual_out, self.out, self.q, self.scales, None, self.variant)
         return L.farn_reduce_add_rmsnorm_ex(arr, self.R, self.residual, self.gamma, self.eps, self.T,
-                                            self.H, self.residual_out, self.out, None, self.variant,
-                                            self.grid_cap)
+                                            self.H, self.residual_out, self.out, None, self.variant)
 
 
 def mk(**kw):
@@ -134,7 +134,6 @@ REJECTIONS = [
     ("q overlaps a partial", dict(quant=True, q=0x10_0000_0000 + 16), ALIAS),
     ("variant 3", dict(variant=3), VARIANT),
     ("variant -1", dict(variant=-1), VARIANT),
-    ("grid_cap < 0", dict(grid_cap=-1), VARIANT),
 ]
 
 

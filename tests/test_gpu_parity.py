@@ -54,15 +54,15 @@ class Uploaded:
         return oracle.reduce_add_rmsnorm(P, res, d["gamma"], EPS, nthreads=8)
 
 
-def run_and_compare(u: Uploaded, quant: bool, variant: str = "auto", grid_cap: int = 0,
+def run_and_compare(u: Uploaded, quant: bool, variant: str = "auto",
                     emit_out: bool = True, rows=None, label: str = ""):
-    say(f"[gpu] {label} R={u.R} T={u.T} H={u.H} quant={quant} variant={variant} cap={grid_cap} "
+    say(f"[gpu] {label} R={u.R} T={u.T} H={u.H} quant={quant} variant={variant} "
         f"emit={emit_out} residual={u.res is not None}")
     if quant:
         ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, emit_out=emit_out,
-                                                          variant=VARIANTS[variant], grid_cap=grid_cap)
+                                                          variant=VARIANTS[variant])
     else:
-        ro, out = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=VARIANTS[variant], grid_cap=grid_cap)
+        ro, out = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=VARIANTS[variant])
     torch.cuda.synchronize()
     rows = np.arange(u.T) if rows is None else np.asarray(rows)
     g_ro = from_dev_bf16(ro)[rows]
@@ -114,8 +114,9 @@ def test_prefill_full_size_sampled(prefill, quant, variant):
 
 
 def test_prefill_full_size_properties(prefill):
-    """Whole-tensor checks at full size: latency and bandwidth paths agree bit for bit on
-    every row, and every output is finite."""
+    """Whole-tensor checks at full size: the latency and bandwidth launch shapes agree bit for
+    bit on every row (their fp64 sums of squares differ only in addition order), and every
+    output is finite."""
     say("[gpu] prefill whole-tensor variant identity")
     a = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_LATENCY)
     b = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_BANDWIDTH)
@@ -207,15 +208,6 @@ def test_empty_T(dev):
 
 
 # ------------------------------------------------------------------ state, order, determinism
-@pytest.mark.parametrize("cap", [1, 2, 3, 7])
-def test_bandwidth_small_grid_reuses_lds(dev, cap):
-    """A tiny grid makes each workgroup stream many rows through its two LDS slots and two
-    register sets; a missing barrier or a slot reused too early shows up as wrong rows."""
-    u = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=20 + cap, T=61), dev)
-    run_and_compare(u, False, "bandwidth", grid_cap=cap, label="cap")
-    run_and_compare(u, True, "bandwidth", grid_cap=cap, label="cap")
-
-
 def test_back_to_back_calls_do_not_leak(dev):
     """Alternate two shapes on one stream without synchronising and check every result."""
     say("[gpu] back-to-back alternating calls")
@@ -244,8 +236,7 @@ def test_back_to_back_calls_do_not_leak(dev):
 def test_deterministic_and_variants_identical(dev):
     u = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=40, T=200), dev)
     say("[gpu] determinism")
-    runs = [F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=v, grid_cap=c)
-            for v, c in ((1, 0), (1, 0), (2, 0), (2, 5))]
+    runs = [F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=v) for v in (1, 1, 2, 2, 0)]
     torch.cuda.synchronize()
     for other in runs[1:]:
         for x, y in zip(runs[0], other):

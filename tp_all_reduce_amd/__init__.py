@@ -48,8 +48,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     base = [pp, i32, vp, vp, f32, i64, i64]
     L.farn_reduce_add_rmsnorm.argtypes = base + [vp, vp, vp]
     L.farn_reduce_add_rmsnorm_quant_group.argtypes = base + [i32, vp, vp, vp, vp, vp]
-    L.farn_reduce_add_rmsnorm_ex.argtypes = base + [vp, vp, vp, i32, i32]
-    L.farn_reduce_add_rmsnorm_quant_group_ex.argtypes = base + [i32, vp, vp, vp, vp, vp, i32, i32]
+    L.farn_reduce_add_rmsnorm_ex.argtypes = base + [vp, vp, vp, i32]
+    L.farn_reduce_add_rmsnorm_quant_group_ex.argtypes = base + [i32, vp, vp, vp, vp, vp, i32]
     L.farn_reduce.argtypes = [pp, i32, i64, i64, vp, vp]
     L.farn_quant_group.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     for fn in EXPORTS[:6]:
@@ -102,7 +102,7 @@ def _stream(device, stream):
 
 
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual_out=None,
-                       out=None, variant: int = VARIANT_AUTO, grid_cap: int = 0, stream=None):
+                       out=None, variant: int = VARIANT_AUTO, stream=None):
     """Sum the R partials (list of bf16 [T,H] device tensors) in rank order in fp32, add the
     residual (or None), round to bf16 -> residual_out, then RMSNorm with gamma -> out.
     residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
@@ -120,7 +120,7 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
     _check_bf16("out", out, (T, H), dev)
     st = _lib.farn_reduce_add_rmsnorm_ex(
         _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
-        _ptr(residual_out), _ptr(out), _stream(dev, stream), variant, grid_cap)
+        _ptr(residual_out), _ptr(out), _stream(dev, stream), variant)
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm")
     return residual_out, out
@@ -129,7 +129,7 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
 def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6, *,
                                    group_size: int = GROUP, emit_out: bool = True, residual_out=None,
                                    out=None, q=None, scales=None, variant: int = VARIANT_AUTO,
-                                   grid_cap: int = 0, stream=None):
+                                   stream=None):
     """The plain call, then per-128-channel E4M3 quant of the bf16 output. Returns
     (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128])."""
     p0 = partials[0]
@@ -154,7 +154,7 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
         raise ValueError("scales: expected contiguous float32 [T, H/group_size]")
     st = _lib.farn_reduce_add_rmsnorm_quant_group_ex(
         _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
-        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant, grid_cap)
+        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
     return residual_out, out, q, scales

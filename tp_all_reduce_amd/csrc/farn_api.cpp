@@ -11,10 +11,13 @@
 
 namespace farn {
 
-RowShape row_shape(int64_t H) {
+RowShape row_shape(int64_t H, int variant) {
     const int64_t nvec = H / 8;
     RowShape s;
-    if (nvec <= 1024) {
+    if (variant == FARN_VARIANT_BANDWIDTH && nvec > 128 && nvec <= 1024) {
+        s.lanes = (int)((((nvec + 1) / 2) + 63) / 64 * 64);  // about NV/2 lanes, two vectors each
+        s.vpl = 2;
+    } else if (nvec <= 1024) {
         s.lanes = (int)(((nvec + 63) / 64) * 64);
         s.vpl = 1;
     } else if (nvec <= 2048) {
@@ -97,30 +100,33 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
     return FARN_OK;
 }
 
-// AUTO rule, set from the measured size sweep on MI355X (R = 8; H = 512 .. 8192; T = 2 ..
-// 32768; plain and FP8; cache-hot and cache-cold): one workgroup per row is as fast
-// or faster at every point from decode (4.4 us for T <= 64) to prefill (6.0 TB/s at
-// T = 8192, H = 7168). The hardware dispatcher keeps two one-row workgroups per CU
-// streaming, while the persistent loop serialises each workgroup's rows behind its
-// barrier. The persistent variant is kept for callers that want a fixed grid.
+// AUTO rule, set from a measured size sweep on MI355X (R = 8; H = 2048, 4096, 7168, 8192;
+// T = 1 .. 8192; plain and FP8; graph replay, cache-hot and cache-cold):
+//   - T < 256 (decode): the widest mapping has the shortest per-row chain and wins
+//     cache-hot at every H (e.g. H = 7168, T = 64: 4.5 us against 5.6 us).
+//   - 4096 < H < 8192 (7168 among them), T >= 256: the narrow mapping wins, by 5% at
+//     T = 8192 with FP8 (214 us against 226 us) and 11% at T = 2048.
+//   - H <= 2048, T >= 2048: the narrow mapping wins by 1-7%.
+//   - H = 4096 and H = 8192: the wide mapping is as fast or faster at every T.
 int select(int R, int64_t T, int64_t H, int quant) {
     (void)R;
-    (void)T;
-    (void)H;
     (void)quant;
+    const int64_t nvec = H / 8;
+    if (nvec <= 128) return FARN_VARIANT_LATENCY;  // one wave per row: no narrower shape
+    if (nvec > 512 && nvec < 1024 && T >= 256) return FARN_VARIANT_BANDWIDTH;
+    if (nvec <= 256 && T >= 2048) return FARN_VARIANT_BANDWIDTH;
     return FARN_VARIANT_LATENCY;
 }
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
                 float eps, int64_t T, int64_t H, int group_size, bool quant, void *residual_out,
-                void *out, void *q, float *scales, void *stream, int variant, int grid_cap) {
-    if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH || grid_cap < 0)
-        return FARN_ERR_VARIANT;
+                void *out, void *q, float *scales, void *stream, int variant) {
+    if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH) return FARN_ERR_VARIANT;
     farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
                            residual_out, out, q, scales);
     if (st != FARN_OK || T == 0) return st;
     if (variant == FARN_VARIANT_AUTO) variant = select(R, T, H, quant ? 1 : 0);
-    if (variant == FARN_VARIANT_LATENCY && T > INT32_MAX) return FARN_ERR_SHAPE;
+    if (T > INT32_MAX) return FARN_ERR_SHAPE;  // one workgroup per row
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
     c.R = R;
@@ -134,7 +140,7 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     c.q = quant ? q : nullptr;
     c.scales = quant ? scales : nullptr;
     c.stream = stream;
-    return farn::launch(c, variant, grid_cap) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, variant) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 // Checks of the standalone all-reduce: partials -> out.
@@ -204,7 +210,7 @@ farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H
     c.T = T;
     c.H = H;
     c.residual_out = out;
-    return farn::launch(c, FARN_VARIANT_LATENCY, 0) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, FARN_VARIANT_LATENCY) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
@@ -219,14 +225,14 @@ farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size
     c.x = x;
     c.q = q;
     c.scales = scales;
-    return farn::launch(c, FARN_VARIANT_LATENCY, 0) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, FARN_VARIANT_LATENCY) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,
                                     const void *gamma, float eps, int64_t T, int64_t H,
                                     void *residual_out, void *out, void *stream) {
     return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
-               nullptr, stream, FARN_VARIANT_AUTO, 0);
+               nullptr, stream, FARN_VARIANT_AUTO);
 }
 
 farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int R,
@@ -235,25 +241,23 @@ farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int
                                                 void *residual_out, void *out, void *q,
                                                 float *scales, void *stream) {
     return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
-               scales, stream, FARN_VARIANT_AUTO, 0);
+               scales, stream, FARN_VARIANT_AUTO);
 }
 
 farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
                                        const void *gamma, float eps, int64_t T, int64_t H,
-                                       void *residual_out, void *out, void *stream, int variant,
-                                       int grid_cap) {
+                                       void *residual_out, void *out, void *stream, int variant) {
     return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
-               nullptr, stream, variant, grid_cap);
+               nullptr, stream, variant);
 }
 
 farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, int R,
                                                    const void *residual, const void *gamma,
                                                    float eps, int64_t T, int64_t H, int group_size,
                                                    void *residual_out, void *out, void *q,
-                                                   float *scales, void *stream, int variant,
-                                                   int grid_cap) {
+                                                   float *scales, void *stream, int variant) {
     return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
-               scales, stream, variant, grid_cap);
+               scales, stream, variant);
 }
 
 int farn_select_variant(int R, int64_t T, int64_t H, int quant) { return select(R, T, H, quant); }
@@ -267,7 +271,7 @@ const char *farn_status_string(int status) {
         case FARN_ERR_ALIAS: return "an output overlaps an input or another output";
         case FARN_ERR_EPS: return "eps is not finite or is negative";
         case FARN_ERR_LAUNCH: return "kernel launch failed";
-        case FARN_ERR_VARIANT: return "unknown variant or negative grid cap";
+        case FARN_ERR_VARIANT: return "unknown variant";
         default: return "unknown status";
     }
 }

@@ -26,16 +26,17 @@ struct Call {
     void *stream;
 };
 
-// Lanes per token row and 16-byte vectors per lane for hidden size H. Both kernel
-// variants use this mapping, so they reduce each row in the same order.
+// Lanes per token row (= workgroup size) and 16-byte vectors per lane for hidden size
+// H and variant (1 = latency: widest mapping; 2 = bandwidth: about half the lanes,
+// two vectors per lane).
 struct RowShape {
     int lanes;  // multiple of 64, <= 1024
     int vpl;    // vectors per lane: 1, 2 or 4
 };
-RowShape row_shape(int64_t H);
+RowShape row_shape(int64_t H, int variant);
 
-// Enqueue the kernel. variant: 1 = latency, 2 = bandwidth (already resolved from AUTO).
-// Returns 0 on success, nonzero when the launch failed.
-int launch(const Call &c, int variant, int grid_cap);
+// Enqueue one workgroup per row. variant: 1 = latency, 2 = bandwidth (already resolved
+// from AUTO; the unfused blocks use 1). Returns 0 on success, nonzero when the launch failed.
+int launch(const Call &c, int variant);
 
 }  // namespace farn

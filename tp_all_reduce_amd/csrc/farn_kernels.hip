@@ -7,28 +7,30 @@
 // fused AllReduce-RMSNorm quant kernel" (sglang #24651 summary: group_size 128,
 // quant of the bf16 normalised output). Here the R partial buffers sit in local HBM.
 //
-// Work mapping (both variants):
-//   A token row of H bf16 is NV = H/8 16-byte vectors. The row is spread over L
-//   lanes (L = multiple of 64, <= 1024) with VPL vectors per lane, lane-strided:
-//   lane l holds vectors l, l+L, l+2L, ... So every load instruction of a wave is
-//   64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is exactly 16
-//   consecutive lanes (one DPP row) of one vector slot.
-//   Per lane: all R+1 loads of a vector are issued before any is consumed; the
+// Work mapping:
+//   One workgroup per token row, grid = T. A row of H bf16 is NV = H/8 16-byte vectors,
+//   spread over L lanes (a multiple of 64, <= 1024) with VPL vectors per lane,
+//   lane-strided: lane l holds vectors l, l+L, l+2L, ... So every load instruction of a
+//   wave is 64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is
+//   exactly 16 consecutive lanes (one DPP row) of one vector slot.
+//   Per lane: the loads of the row's slots are issued before any is consumed; the
 //   partials are summed in fp32 in rank order, the residual added last, the sum
 //   rounded to bf16 (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
 //   per wave through LDS -> every wave adds the per-wave values in wave order; the
 //   normalisation product is fp64 too, rounded once to bf16. The row never passes
 //   through LDS; only one double per wave does.
-//   The order of that reduction depends only on (H, L, VPL), which both variants
-//   share, so both give bit-identical results.
 //
-// Variants:
-//   latency   - one workgroup per row (grid = T). Every wave issues its loads at once;
-//               used while T is small (decode).
-//   bandwidth - persistent: grid = resident workgroups; each streams rows t, t+G, ...
-//               and issues the loads of its next row before reducing the current
-//               one, so each CU always has a row of loads in flight (prefill).
+// Two launch shapes of the same kernel (chosen by the host from T and H):
+//   latency   - the widest row mapping (L up to 1024, one vector per lane up to H =
+//               8192): the fewest dependent instructions per lane, for small T where
+//               a row's own latency is the call's latency (decode).
+//   bandwidth - a narrow mapping (L about NV/2, two vectors per lane, both issued up
+//               front): workgroups of about 7 waves, so several rows share a CU and one
+//               row's arithmetic overlaps another's loads (prefill). On MI355X this
+//               moves the FP8 prefill call from 225 to 214 us.
+// The fp64 statistics make the two shapes agree bit for bit in practice (their sums
+// of squares differ only in the order of fp64 additions).
 //
 // No MFMA: nothing here is a contraction; the op is HBM-bound (about 0.5 flop per
 // byte against a ridge of ~20 flop/byte).
@@ -326,8 +328,10 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
     if constexpr (QUANT) quant_slot(o, r_q, r_sc, off);
 }
 
-// Whole row t with the loads of slot 0 already issued into `in0` (VPL > 1 loads and
-// reduces the other slots one after the other, to bound register use).
+// Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
+// lane the second slot's loads are issued before the first is reduced; with four (rows
+// beyond 16384 channels) the slots are loaded and reduced one after the other, to bound
+// register use.
 template <int R, int VPL, bool QUANT>
 __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
                                        const Params &k, int64_t t, double *slot) {
@@ -338,12 +342,19 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const rsrc_t r_ro = row_rsrc(k.res_out, ro, rb);
     double ss = 0.0;
     u32x4 yb[VPL];
-    yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
+    if constexpr (VPL == 2) {
+        SlotIn<R> in1;
+        load_slot<R>(in1, k, t, off0 + L16);
+        yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
+        yb[1] = reduce_slot<R>(in1, k, r_ro, off0 + L16, ss);
+    } else {
+        yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) {
-        SlotIn<R> in;
-        load_slot<R>(in, k, t, off0 + v * L16);
-        yb[v] = reduce_slot<R>(in, k, r_ro, off0 + v * L16, ss);
+        for (int v = 1; v < VPL; ++v) {
+            SlotIn<R> in;
+            load_slot<R>(in, k, t, off0 + v * L16);
+            yb[v] = reduce_slot<R>(in, k, r_ro, off0 + v * L16, ss);
+        }
     }
     const double rstd = row_rstd(ss, k, slot);
     const rsrc_t r_out = row_rsrc(k.out, k.out ? ro : 0, k.out ? rb : 0);
@@ -363,7 +374,7 @@ __device__ __forceinline__ void load_gamma(u32x4 (&gam)[VPL], const Params &k) {
 
 // ---------------------------------------------------------------- kernels
 template <int R, int VPL, bool QUANT>
-__global__ __launch_bounds__(1024) void farn_latency(const Params k) {
+__global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     __shared__ double slot[kMaxWaves];
     const int64_t t = blockIdx.x;
     SlotIn<R> in;
@@ -371,32 +382,6 @@ __global__ __launch_bounds__(1024) void farn_latency(const Params k) {
     u32x4 gam[VPL];
     load_gamma<VPL>(gam, k);
     do_row<R, VPL, QUANT>(in, gam, k, t, slot);
-}
-
-template <int R, int VPL, bool QUANT>
-__global__ __launch_bounds__(1024) void farn_bandwidth(const Params k) {
-    __shared__ double slots[2][kMaxWaves];
-    const int64_t G = gridDim.x;
-    int64_t t = blockIdx.x;
-    if (t >= k.T) return;
-    u32x4 gam[VPL];
-    load_gamma<VPL>(gam, k);
-    const uint32_t off0 = threadIdx.x * 16u;
-    SlotIn<R> a, b;
-    load_slot<R>(a, k, t, off0);
-    // Two register sets, alternated by hand so neither is copied (a copy would wait for
-    // the loads in flight): the first slot of row t+G loads while row t finishes. The
-    // prefetch past the last row has 0 records and moves no data.
-    while (true) {
-        load_slot<R>(b, k, t + G, off0);
-        do_row<R, VPL, QUANT>(a, gam, k, t, slots[0]);
-        t += G;
-        if (t >= k.T) break;
-        load_slot<R>(a, k, t + G, off0);
-        do_row<R, VPL, QUANT>(b, gam, k, t, slots[1]);
-        t += G;
-        if (t >= k.T) break;
-    }
 }
 
 // Unfused building blocks (the compositions the fused call replaces): the all-reduce
@@ -443,10 +428,7 @@ typedef void (*KernelFn)(const Params);
 
 template <int R, bool Q>
 struct Row {
-    static constexpr KernelFn lat[3] = {farn_latency<R, 1, Q>, farn_latency<R, 2, Q>,
-                                        farn_latency<R, 4, Q>};
-    static constexpr KernelFn bw[3] = {farn_bandwidth<R, 1, Q>, farn_bandwidth<R, 2, Q>,
-                                       farn_bandwidth<R, 4, Q>};
+    static constexpr KernelFn fn[3] = {farn_rows<R, 1, Q>, farn_rows<R, 2, Q>, farn_rows<R, 4, Q>};
 };
 
 template <int R>
@@ -468,10 +450,10 @@ KernelFn pick_reduce(int R, int vi) {
 }
 
 template <bool Q>
-KernelFn pick(int variant, int R, int vi) {
+KernelFn pick(int R, int vi) {
     switch (R) {
 #define FARN_CASE(n) \
-    case n: return variant == 1 ? Row<n, Q>::lat[vi] : Row<n, Q>::bw[vi];
+    case n: return Row<n, Q>::fn[vi];
         FARN_CASE(1) FARN_CASE(2) FARN_CASE(3) FARN_CASE(4)
         FARN_CASE(5) FARN_CASE(6) FARN_CASE(7) FARN_CASE(8)
 #undef FARN_CASE
@@ -479,33 +461,20 @@ KernelFn pick(int variant, int R, int vi) {
     }
 }
 
-int resident_grid(KernelFn fn, int lanes) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, lanes, 0) != hipSuccess)
-        return 0;
-    if (per_cu < 1) per_cu = 1;
-    return cus * per_cu;
-}
-
 }  // namespace
 
 namespace farn {
 
-int launch(const Call &c, int variant, int grid_cap) {
-    const RowShape rs = row_shape(c.H);
+int launch(const Call &c, int variant) {
+    const RowShape rs = row_shape(c.H, c.kind == Kind::kFused ? variant : 1);
     const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
     KernelFn fn = nullptr;
     if (c.kind == Kind::kReduce) {
         fn = pick_reduce(c.R, vi);
-        variant = 1;
     } else if (c.kind == Kind::kQuant) {
         fn = kQuantRows[vi];
-        variant = 1;
     } else {
-        const bool quant = c.q != nullptr;
-        fn = quant ? pick<true>(variant, c.R, vi) : pick<false>(variant, c.R, vi);
+        fn = c.q != nullptr ? pick<true>(c.R, vi) : pick<false>(c.R, vi);
     }
     if (!fn) return 1;
 
@@ -523,18 +492,7 @@ int launch(const Call &c, int variant, int grid_cap) {
     k.ngroups = (int)(c.H / 128);
     k.h = (double)c.H;
     k.eps = c.eps;
-
-    int64_t grid;
-    if (variant == 1) {
-        grid = c.T;
-    } else {
-        grid = resident_grid(fn, rs.lanes);
-        if (grid <= 0) return 1;
-        if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
-        if (grid > c.T) grid = c.T;
-    }
-    hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3((uint32_t)rs.lanes), 0,
-                       (hipStream_t)c.stream, k);
+    hipLaunchKernelGGL(fn, dim3((uint32_t)c.T), dim3((uint32_t)rs.lanes), 0, (hipStream_t)c.stream, k);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
