@@ -60,6 +60,15 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_quant_group.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                      ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
     L.oracle_quant_group.restype = ctypes.c_int
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    L.oracle_e2m1_from_double.argtypes = [ctypes.c_double]
+    L.oracle_e2m1_from_double.restype = ctypes.c_uint8
+    L.oracle_mxfp4.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, u8p, u8p]
+    L.oracle_mxfp4.restype = ctypes.c_int
+    L.oracle_reduce_add_rmsnorm_mxfp4.argtypes = [
+        ctypes.POINTER(u16p), ctypes.c_int, u16p, u16p, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+        u16p, u16p, u8p, u8p, ctypes.c_int]
+    L.oracle_reduce_add_rmsnorm_mxfp4.restype = ctypes.c_int
     return L
 
 
@@ -192,3 +201,40 @@ def quant_group(x, group: int = 128):
     if rc != 0:
         raise RuntimeError("oracle_quant_group failed")
     return q, scales
+
+
+def e2m1_from_double(x: float) -> int:
+    return int(lib().oracle_e2m1_from_double(float(x)))
+
+
+def mxfp4(x):
+    """MXFP4 of a bf16 [T,H] array (H % 32 == 0): (q uint8 [T, H/2] two E2M1 codes per byte,
+    element 2i in the low nibble; scales uint8 [T, H/32] E8M0)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 32), np.uint8)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    if lib().oracle_mxfp4(_u16(x), T, H, q.ctypes.data_as(u8), sc.ctypes.data_as(u8)) != 0:
+        raise RuntimeError("oracle_mxfp4 failed")
+    return q, sc
+
+
+def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, emit_out: bool = True,
+                             nthreads: int = 1):
+    """Fused call with MXFP4 output: (residual_out, out or None, q [T,H/2] u8, scales [T,H/32] u8)."""
+    plist = _partials_list(partials)
+    T, H = plist[0].shape
+    g = np.ascontiguousarray(gamma, dtype=np.uint16)
+    res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
+    res_out = np.empty((T, H), np.uint16)
+    out = np.empty((T, H), np.uint16) if emit_out else None
+    q = np.empty((T, H // 2), np.uint8)
+    sc = np.empty((T, H // 32), np.uint8)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    rc = lib().oracle_reduce_add_rmsnorm_mxfp4(
+        _ptr_array(plist), len(plist), None if res is None else _u16(res), _u16(g), eps, T, H,
+        _u16(res_out), None if out is None else _u16(out), q.ctypes.data_as(u8), sc.ctypes.data_as(u8), nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_reduce_add_rmsnorm_mxfp4 failed")
+    return res_out, out, q, sc

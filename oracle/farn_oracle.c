@@ -309,3 +309,87 @@ int oracle_quant_group(const uint16_t *x, int64_t T, int64_t H, int group, uint8
     }
     return 0;
 }
+
+/*
+ * MXFP4 output (the third one-stage variant named in "Fix: add missing end_sync barrier
+ * in fused allreduce+rmsnorm kernel", Copilot overview: the MXFP4 1-stage variant). The
+ * pages name the format only; it is written here from the OCP Microscaling Formats (MX)
+ * v1.0 specification:
+ *   - blocks of 32 consecutive elements along H share one scale X = 2^s of type E8M0
+ *     (an 8-bit biased exponent, bias 127, 0xFF = NaN);
+ *   - s = floor(log2(max |V_i|)) - emax, emax = 2 for the FP4 E2M1 element type (its
+ *     largest normal is 6 = 1.5 * 2^2), clamped to the E8M0 range [-127, 127];
+ *   - each element P_i = V_i / X rounded to E2M1 (1 sign, 2 exponent bits with bias 1,
+ *     1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), round to nearest even, magnitudes
+ *     above 6 clamped to 6.
+ * Readings (the spec or the pages leave these open): V is the bf16 `out`; an all-zero
+ * block gets s = -127 (byte 0x00) and zero codes; a block holding a NaN gets the NaN
+ * scale 0xFF and zero codes; two codes per byte, element 2i in the low nibble; scales
+ * are bytes [T, H/32] row-major.
+ */
+
+/* E2M1 code of a binary64 value, one rounding to nearest even, saturating to +-6. */
+uint8_t oracle_e2m1_from_double(double x) {
+    const uint8_t sign = signbit(x) ? 0x8u : 0u;
+    double a = fabs(x);
+    if (isnan(x)) return 0; /* not reached: NaN blocks are handled by the caller */
+    if (a >= 6.0) return (uint8_t)(sign | 0x7u);
+    /* quantum: 0.5 below 2, 1 in [2,4), 2 in [4,8) */
+    double quantum = a < 2.0 ? 0.5 : (a < 4.0 ? 1.0 : 2.0);
+    double r = nearbyint(a / quantum) * quantum; /* ties to even multiple of the quantum */
+    static const double values[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    for (uint8_t c = 0; c < 8; ++c)
+        if (values[c] == r) return (uint8_t)(sign | c);
+    return (uint8_t)(sign | 0x7u); /* r == 8 (from [7, 8)): clamp to 6 */
+}
+
+/* MXFP4 of a bf16 [T,H] input: q [T, H/2] bytes (two codes each), scales [T, H/32] E8M0 bytes. */
+int oracle_mxfp4(const uint16_t *x, int64_t T, int64_t H, uint8_t *q, uint8_t *scales) {
+    if (!x || !q || !scales || T < 0 || H < 32 || H % 32 != 0) return -1;
+    const int64_t B = H / 32;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < B; ++b) {
+            const uint16_t *v = x + t * H + b * 32;
+            double amax = 0.0;
+            int has_nan = 0;
+            for (int i = 0; i < 32; ++i) {
+                double a = fabs(bf16_to_double(v[i]));
+                if (isnan(a)) has_nan = 1;
+                else if (a > amax) amax = a;
+            }
+            uint8_t codes[32];
+            if (has_nan) {
+                scales[t * B + b] = 0xFFu;
+                for (int i = 0; i < 32; ++i) codes[i] = 0;
+            } else if (amax == 0.0) {
+                scales[t * B + b] = 0x00u;
+                for (int i = 0; i < 32; ++i) codes[i] = 0;
+            } else {
+                int e2;
+                frexp(amax, &e2);       /* amax in [2^(e2-1), 2^e2) */
+                int s = (e2 - 1) - 2;   /* floor(log2 amax) - emax */
+                if (s < -127) s = -127;
+                if (s > 127) s = 127;
+                scales[t * B + b] = (uint8_t)(s + 127);
+                for (int i = 0; i < 32; ++i) codes[i] = oracle_e2m1_from_double(ldexp(bf16_to_double(v[i]), -s));
+            }
+            for (int i = 0; i < 16; ++i)
+                q[t * (H / 2) + b * 16 + i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+        }
+    }
+    return 0;
+}
+
+/* The fused call with MXFP4 output: steps 1-5, then MXFP4 of the bf16 out. `out` may be NULL. */
+int oracle_reduce_add_rmsnorm_mxfp4(const uint16_t *const *partials, int R, const uint16_t *residual,
+                                    const uint16_t *gamma, float eps, int64_t T, int64_t H,
+                                    uint16_t *residual_out, uint16_t *out, uint8_t *q, uint8_t *scales,
+                                    int nthreads) {
+    if (H % 32 != 0 || !q || !scales) return -1;
+    uint16_t *o = out ? out : (uint16_t *)malloc((size_t)(T * H > 0 ? T * H : 1) * sizeof(uint16_t));
+    if (!o) return -2;
+    int rc = oracle_reduce_add_rmsnorm(partials, R, residual, gamma, eps, T, H, residual_out, o, nthreads);
+    if (rc == 0) rc = oracle_mxfp4(o, T, H, q, scales);
+    if (!out) free(o);
+    return rc;
+}

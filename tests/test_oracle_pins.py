@@ -406,6 +406,97 @@ def check_quant_alone():
             assert q[t, h] == e4m3fn_nearest(v, negative_zero=(xb[t, h] == 0x8000)), (t, h)
 
 
+# ============================================================================ MXFP4
+E2M1_VALUES = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3),
+               Fraction(4), Fraction(6)]
+
+
+def e2m1_nearest(v: Fraction) -> int:
+    """E2M1 code nearest to v by search over the 8 magnitudes; ties to the even code; > 6 clamps."""
+    sign = 0x8 if v < 0 else 0
+    a = min(abs(v), Fraction(6))
+    best = None
+    for c, val in enumerate(E2M1_VALUES):
+        d = abs(a - val)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return sign | best[1]
+
+
+def check_e2m1_encoder():
+    """Every finite bf16 value against the nearest-code search, and the OCP MX code table."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        f = bf16_bits_to_float(bits).astype(np.float64)
+    for x in f[np.isfinite(f)][::7]:
+        got = oracle.e2m1_from_double(float(x))
+        want = e2m1_nearest(Fraction(float(x)))
+        if x == 0 and np.signbit(x):
+            want = 0x8
+        assert got == want, (x, got, want)
+    for value, code in read_value_code_table("e2m1_codes.txt"):
+        assert oracle.e2m1_from_double(value) == code, (value, code)
+
+
+def _decode_e2m1(c):
+    return (-1 if c & 0x8 else 1) * float(E2M1_VALUES[c & 0x7])
+
+
+def check_mxfp4_blocks():
+    """Scales and codes of whole blocks: 2^(s+2) <= amax < 2^(s+3); the block maximum maps to 4 or
+    6; dequantised values within half a step (or clamped at 6); zero and NaN blocks; element 2i in
+    the low nibble."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, 256)).astype(np.float32) * np.float32(3.0)
+    x[:, rng.choice(256, 5, replace=False)] *= 20
+    x[1, 32:64] = 0.0
+    x[2, 64:96] *= np.float32(2.0 ** -100)
+    xb = f2b(x)
+    xb[3, 100] = 0x7FC0  # NaN in block 3 of row 3
+    q, sc = oracle.mxfp4(xb)
+    v = bf16_bits_to_float(xb).astype(np.float64)
+    for t in range(6):
+        for b in range(8):
+            blk = v[t, 32 * b:32 * b + 32]
+            codes = [(q[t, 16 * b + i // 2] >> (4 * (i % 2))) & 0xF for i in range(32)]
+            if np.isnan(blk).any():
+                assert sc[t, b] == 0xFF
+                continue
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert sc[t, b] == 0 and all(c == 0 for c in codes)
+                continue
+            s = int(sc[t, b]) - 127
+            assert 2.0 ** (s + 2) <= amax < 2.0 ** (s + 3), (t, b, s, amax)
+            X = 2.0 ** s
+            top = int(np.argmax(np.abs(blk)))
+            assert codes[top] & 0x7 in (6, 7)
+            for i in range(32):
+                r = blk[i] / X
+                step = 0.5 if abs(r) < 2 else (1.0 if abs(r) < 4 else 2.0)
+                err = abs(_decode_e2m1(codes[i]) - r)
+                assert err <= step / 2 or (abs(r) > 6 and codes[i] & 0x7 == 7), (t, b, i, r, codes[i])
+    # nibble order: a block whose element 0 is the maximum and element 1 zero
+    y = np.zeros((1, 32), np.float32)
+    y[0, 0] = 4.0
+    q1, s1 = oracle.mxfp4(f2b(y))
+    assert q1[0, 0] == 0x06 and s1[0, 0] == 127
+
+
+def check_mxfp4_fused_consistency():
+    """The fused MXFP4 call's residual_out / out equal the plain call's, and its codes equal the
+    MXFP4 of that out; with out not emitted, the codes are unchanged."""
+    d = make_inputs(CONFIGS["decode_fp8"], seed=33, T=5, H=512)
+    ro, out, q, sc = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS)
+    ro2, out2 = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS)
+    assert np.array_equal(ro, ro2) and np.array_equal(out, out2)
+    q2, sc2 = oracle.mxfp4(out)
+    assert np.array_equal(q, q2) and np.array_equal(sc, sc2)
+    _, none, q3, sc3 = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS,
+                                                      emit_out=False)
+    assert none is None and np.array_equal(q, q3) and np.array_equal(sc, sc3)
+
+
 ALL_CHECKS = [
     check_bf16_encoder_vs_torch_cast, check_bf16_golden_rounding_points, check_bf16_encoder_exact_on_doubles,
     check_e4m3_encoder_exhaustive_bf16, check_e4m3_encoder_exact_near_ties, check_e4m3_golden_codes,
@@ -416,6 +507,7 @@ ALL_CHECKS = [
     check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_dequant_bound,
     check_quant_zero_group_and_consistency, check_in_place_residual,
     check_reduce_alone, check_quant_alone,
+    check_e2m1_encoder, check_mxfp4_blocks, check_mxfp4_fused_consistency,
 ]
 
 
@@ -465,6 +557,13 @@ MUTANTS = [
     ("quant_alone_scale_240", "float scale = (float)(amax / 448.0);\n            scales[t * G + g] = scale;",
      "float scale = (float)(amax / 240.0);\n            scales[t * G + g] = scale;"),
     ("quant_alone_wrong_group_base", "const uint16_t *o = x + t * H + g * group;", "const uint16_t *o = x + t * H;"),
+    ("mx_emax_3", "int s = (e2 - 1) - 2;", "int s = (e2 - 1) - 3;"),
+    ("mx_nibbles_swapped", "(uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4))", "(uint8_t)(codes[2 * i + 1] | (codes[2 * i] << 4))"),
+    ("mx_no_saturation", "if (a >= 6.0) return (uint8_t)(sign | 0x7u);", "if (a >= 1e30) return (uint8_t)(sign | 0x7u);",
+     "return (uint8_t)(sign | 0x7u); /* r == 8", "return (uint8_t)(sign | 0x0u); /* r == 8"),
+    ("mx_truncates", "double r = nearbyint(a / quantum) * quantum; /* ties to even multiple of the quantum */",
+     "double r = floor(a / quantum) * quantum;"),
+    ("mx_block_16", "const uint16_t *v = x + t * H + b * 32;", "const uint16_t *v = x + t * H + b * 16;"),
 ]
 
 
