@@ -56,7 +56,8 @@ typedef enum farn_status {
     FARN_OK = 0,
     FARN_ERR_NULL = 1,    /* a required pointer is NULL */
     FARN_ERR_SHAPE = 2,   /* R not in [1, FARN_MAX_R]; T < 0; H <= 0, H % 8 != 0 or
-                             H > FARN_MAX_H; quant: group_size != 128 or H % 128 != 0 */
+                             H > FARN_MAX_H; FP8 quant: group_size != 128 or H % 128 != 0;
+                             MXFP4: H % 32 != 0 */
     FARN_ERR_ALIGN = 3,   /* a bf16 / q buffer is not 16-byte aligned, or scales not 4-byte aligned */
     FARN_ERR_ALIAS = 4,   /* an output overlaps an input or another output (the one allowed
                              overlap: residual_out == residual exactly, in place) */
@@ -72,6 +73,8 @@ typedef enum farn_status {
 #define FARN_MAX_H 32768
 /* Quant group along H ("per-1x128", group_size=128 in the sglang #24651 summary). */
 #define FARN_GROUP 128
+/* MXFP4 block along H (OCP Microscaling Formats (MX) v1.0: 32 elements per shared scale). */
+#define FARN_MX_BLOCK 32
 #define FARN_ABI_VERSION 2
 
 /*
@@ -104,6 +107,24 @@ farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int
                                                 void *residual_out, void *out, void *q,
                                                 float *scales, void *stream);
 
+/*
+ * MXFP4 call: the plain call, then MXFP4 of the bf16 output - the third one-stage
+ * variant of the fused kernel ("Fix: add missing end_sync barrier in fused
+ * allreduce+rmsnorm kernel", Copilot overview, names it). Format from the OCP
+ * Microscaling Formats (MX) v1.0 specification: per row and block b of 32 channels,
+ *   scales[t,b] = E8M0 byte s + 127, s = floor(log2(max |out|)) - 2, clamped to
+ *                 [-127, 127]; 0xFF (NaN) if the block holds a NaN; 0x00 if it is all zero
+ *   code        = E2M1 of out / 2^s, round to nearest even, magnitudes above 6 clamped to 6
+ *                 (0 for NaN and zero blocks)
+ *   q[t, i]     = code of channel 2i in bits 0-3, code of channel 2i+1 in bits 4-7
+ *   H % 32 == 0; q device uint8 [T, H/2] (16-byte aligned); scales device uint8 [T, H/32];
+ *   out device bf16 [T,H] or NULL (bf16 output not written).
+ */
+farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, const void *residual,
+                                          const void *gamma, float eps, int64_t T, int64_t H,
+                                          void *residual_out, void *out, void *q, void *scales,
+                                          void *stream);
+
 /* Launch shapes of the one kernel (one workgroup per token row). AUTO picks by size
    (farn_select_variant). LATENCY: the widest row mapping (up to 1024 lanes, one 16-byte
    vector per lane up to H = 8192), the shortest per-row chain, for small T. BANDWIDTH:
@@ -125,6 +146,10 @@ farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, 
                                                    float eps, int64_t T, int64_t H, int group_size,
                                                    void *residual_out, void *out, void *q,
                                                    float *scales, void *stream, int variant);
+farn_status farn_reduce_add_rmsnorm_mxfp4_ex(const void *const *partials, int R, const void *residual,
+                                             const void *gamma, float eps, int64_t T, int64_t H,
+                                             void *residual_out, void *out, void *q, void *scales,
+                                             void *stream, int variant);
 
 /*
  * Unfused building blocks: the kernels the fused calls replace. The sglang #24651

@@ -42,8 +42,9 @@ def compare_bf16(name: str, gpu_bits, ref_bits) -> dict:
     both_nan = np.isnan(g) & np.isnan(r)
     with np.errstate(invalid="ignore"):
         err = np.where(both_nan | (g == r), 0.0, np.abs(g - r))  # g == r also covers equal infinities
-    tol = BF16_REL * np.abs(r) + BF16_ABS
-    bad = ~(err <= tol)
+    with np.errstate(invalid="ignore"):
+        tol = BF16_REL * np.abs(r) + BF16_ABS
+        bad = ~(err <= tol) & ~both_nan  # a NaN reference has a NaN tolerance
     ne = (gpu_bits != ref_bits) & ~both_nan & ~((g == 0) & (r == 0))
     with np.errstate(invalid="ignore"):
         rel = np.where(np.abs(r) > 0, err / np.maximum(np.abs(r), 1e-30), err)
@@ -93,4 +94,31 @@ def within_tolerance(rep_ro: dict, rep_out: dict | None, rep_fp8: dict | None,
             msgs.append(f"q: a code differs by {rep_fp8['max_code_step']} steps")
         if rep_fp8["max_scale_rel_err"] > SCALE_REL:
             msgs.append(f"scales: rel err {rep_fp8['max_scale_rel_err']:.2e}")
+    return (not msgs), "; ".join(msgs)
+
+
+def compare_mxfp4(gpu_q, ref_q, gpu_s, ref_s) -> dict:
+    """MXFP4 codes (two per byte) and E8M0 scale bytes. Tolerance, by the same reading as the
+    E4M3 codes: at most 0.1% of codes differ, each by one step of the E2M1 grid; scale bytes
+    differ on at most 0.1% of blocks, by one exponent."""
+    gq, rq = np.asarray(gpu_q, np.uint8), np.asarray(ref_q, np.uint8)
+    g = np.stack([gq & 0xF, gq >> 4], axis=-1).reshape(-1).astype(np.int32)
+    r = np.stack([rq & 0xF, rq >> 4], axis=-1).reshape(-1).astype(np.int32)
+    rank = lambda c: np.where(c & 0x8, -(c & 0x7), c & 0x7)
+    zero = ((g & 0x7) == 0) & ((r & 0x7) == 0)
+    diff = (g != r) & ~zero
+    step = np.where(zero, 0, np.abs(rank(g) - rank(r)))
+    gs, rs = np.asarray(gpu_s, np.int32), np.asarray(ref_s, np.int32)
+    sdiff = gs != rs
+    return {"n": int(g.size), "n_code_diff": int(diff.sum()), "frac_code_diff": float(diff.mean()) if g.size else 0.0,
+            "max_code_step": int(step.max()) if step.size else 0, "n_scales": int(gs.size),
+            "n_scale_diff": int(sdiff.sum()), "max_scale_step": int(np.abs(gs - rs).max()) if gs.size else 0}
+
+
+def mxfp4_within_tolerance(rep: dict) -> tuple[bool, str]:
+    msgs = []
+    if rep["frac_code_diff"] > FP8_MAX_FRAC or rep["max_code_step"] > 1:
+        msgs.append(f"mxfp4 codes: {rep['n_code_diff']} differ, max step {rep['max_code_step']}")
+    if rep["n_scale_diff"] > FP8_MAX_FRAC * max(1, rep["n_scales"]) or rep["max_scale_step"] > 1:
+        msgs.append(f"mxfp4 scales: {rep['n_scale_diff']} differ, max step {rep['max_scale_step']}")
     return (not msgs), "; ".join(msgs)

@@ -44,6 +44,7 @@ def test_header_constants_match_binding():
     assert int(consts["FARN_MAX_R"]) == F.MAX_R
     assert int(consts["FARN_MAX_H"]) == F.MAX_H
     assert int(consts["FARN_GROUP"]) == F.GROUP
+    assert int(consts["FARN_MX_BLOCK"]) == F.MX_BLOCK
     assert int(consts["FARN_ABI_VERSION"]) == F.abi_version()
     names = re.findall(r"(FARN_(?:OK|ERR_[A-Z]+)) = (\d+)", text)
     assert {int(v): k for k, v in names} == F.STATUS
@@ -202,3 +203,29 @@ def test_unfused_rejections(what, fn, want):
 def test_unfused_empty():
     assert reduce_call(T=0, out=0) == OK
     assert quant_call(T=0, x=0, q=0, scales=0) == OK
+
+
+def mx_call(H=256, q=0x10_3000_0000, scales=0x10_4000_0000, out=0x10_5000_0000, T=4):
+    c = FakeCall(T=T, H=H)
+    arr = (ctypes.c_void_p * 2)(*c.partials)
+    return L.farn_reduce_add_rmsnorm_mxfp4_ex(arr, 2, c.residual, c.gamma, 1e-6, T, H, c.residual_out, out,
+                                              q, scales, None, 0)
+
+
+MX_REJECTIONS = [
+    ("mxfp4 H % 32", lambda: mx_call(H=264), SHAPE),
+    ("mxfp4 q NULL", lambda: mx_call(q=0), NULL),
+    ("mxfp4 scales NULL", lambda: mx_call(scales=0), NULL),
+    ("mxfp4 q misaligned", lambda: mx_call(q=0x10_3000_0008), ALIGN),
+    ("mxfp4 q overlaps scales", lambda: mx_call(scales=0x10_3000_0000 + 100), ALIAS),
+    ("mxfp4 scales overlap out", lambda: mx_call(scales=0x10_5000_0000 + 7), ALIAS),
+]
+
+
+@pytest.mark.parametrize("what,fn,want", MX_REJECTIONS, ids=[r[0] for r in MX_REJECTIONS])
+def test_mxfp4_rejections(what, fn, want):
+    assert fn() == want, what
+
+
+def test_mxfp4_accepts_byte_aligned_scales_and_null_out():
+    assert mx_call(T=0, scales=0x10_4000_0001, out=0) == OK

@@ -18,7 +18,8 @@ import torch
 import oracle
 import tp_all_reduce_amd as F
 from gen import CONFIGS, make_inputs, sweep_config
-from parity import compare_bf16, compare_fp8, from_dev_bf16, to_dev_bf16, within_tolerance
+from parity import (compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16, mxfp4_within_tolerance,
+                    to_dev_bf16, within_tolerance)
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -369,3 +370,57 @@ def test_quant_alone_shapes(dev, H):
     torch.cuda.synchronize()
     rq, rs = oracle.quant_group(xb)
     assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+
+
+
+# ------------------------------------------------------------------ MXFP4 output
+def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label=""):
+    say(f"[gpu] mxfp4 {label} R={u.R} T={u.T} H={u.H} variant={variant} emit={emit_out}")
+    ro, out, q, sc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, emit_out=emit_out, variant=VARIANTS[variant])
+    torch.cuda.synchronize()
+    rows = np.arange(u.T) if rows is None else np.asarray(rows)
+    d = u.d
+    ref = oracle.reduce_add_rmsnorm_mxfp4(d["partials"][:, rows, :],
+                                          None if u.res is None else d["residual"][rows], d["gamma"], EPS,
+                                          emit_out, nthreads=8)
+    ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro)[rows], ref[0]),
+                               None if out is None else compare_bf16("out", from_dev_bf16(out)[rows], ref[1]), None)
+    assert ok, f"{label}: {why}"
+    rep = compare_mxfp4(q.cpu().numpy()[rows], ref[2], sc.cpu().numpy()[rows], ref[3])
+    ok, why = mxfp4_within_tolerance(rep)
+    assert ok, f"{label}: {why} {rep}"
+    return rep
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("name", ["tiny", "decode_ds", "decode_fp8"])
+def test_mxfp4_configs(dev, name, variant):
+    u = Uploaded(make_inputs(CONFIGS[name], seed=90), dev)
+    rep = run_mxfp4(u, variant, label=name)
+    assert rep["n_code_diff"] == 0 and rep["n_scale_diff"] == 0  # bit-exact in practice
+
+
+@pytest.mark.parametrize("variant", ["latency", "bandwidth"])
+def test_mxfp4_prefill_sampled(prefill, variant):
+    run_mxfp4(prefill, variant, rows=_sample_rows(prefill.T), label="prefill")
+
+
+@pytest.mark.parametrize("H", [32, 96, 160, 1024, 8224, 16384, 32768])
+def test_mxfp4_edge_H(dev, H):
+    u = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=H, R=3, T=5, H=H), dev)
+    for variant in VARIANTS:
+        run_mxfp4(u, variant, label=f"H{H}")
+
+
+def test_mxfp4_no_residual_no_out_and_special_blocks(dev):
+    d = make_inputs(CONFIGS["tiny"], seed=91, R=2, T=4, H=256)
+    d["partials"][1, 1, 32:64] = d["partials"][0, 1, 32:64] ^ 0x8000   # row 1 block 1 cancels ...
+    d["partials"][1, 2, 70] = 0x7FC0                                     # row 2 has a NaN
+    u = Uploaded(d, dev, residual=False)                                 # ... with no residual: zero block
+    for variant in VARIANTS:
+        run_mxfp4(u, variant, emit_out=False, label="special")
+    ro, out, q, sc = F.reduce_add_rmsnorm_mxfp4(u.P, None, u.g, EPS)
+    torch.cuda.synchronize()
+    scn = sc.cpu().numpy()
+    assert scn[1, 1] == 0 and np.all(q.cpu().numpy()[1, 16:32] == 0)
+    assert np.all(scn[2] == 0xFF)  # the NaN makes the whole row's out NaN

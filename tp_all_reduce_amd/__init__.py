@@ -25,10 +25,11 @@ OK = 0
 STATUS = {0: "FARN_OK", 1: "FARN_ERR_NULL", 2: "FARN_ERR_SHAPE", 3: "FARN_ERR_ALIGN",
           4: "FARN_ERR_ALIAS", 5: "FARN_ERR_EPS", 6: "FARN_ERR_LAUNCH", 7: "FARN_ERR_VARIANT"}
 VARIANT_AUTO, VARIANT_LATENCY, VARIANT_BANDWIDTH = 0, 1, 2
-MAX_R, MAX_H, GROUP = 8, 32768, 128
+MAX_R, MAX_H, GROUP, MX_BLOCK = 8, 32768, 128, 32
 EXPORTS = ("farn_reduce_add_rmsnorm", "farn_reduce_add_rmsnorm_quant_group",
            "farn_reduce_add_rmsnorm_ex", "farn_reduce_add_rmsnorm_quant_group_ex",
            "farn_reduce", "farn_quant_group",
+           "farn_reduce_add_rmsnorm_mxfp4", "farn_reduce_add_rmsnorm_mxfp4_ex",
            "farn_select_variant", "farn_status_string", "farn_abi_version")
 
 
@@ -52,7 +53,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.farn_reduce_add_rmsnorm_quant_group_ex.argtypes = base + [i32, vp, vp, vp, vp, vp, i32]
     L.farn_reduce.argtypes = [pp, i32, i64, i64, vp, vp]
     L.farn_quant_group.argtypes = [vp, i64, i64, i32, vp, vp, vp]
-    for fn in EXPORTS[:6]:
+    L.farn_reduce_add_rmsnorm_mxfp4.argtypes = base + [vp, vp, vp, vp, vp]
+    L.farn_reduce_add_rmsnorm_mxfp4_ex.argtypes = base + [vp, vp, vp, vp, vp, i32]
+    for fn in EXPORTS[:8]:
         getattr(L, fn).restype = i32
     L.farn_select_variant.argtypes = [i32, i64, i64, i32]
     L.farn_select_variant.restype = i32
@@ -188,3 +191,36 @@ def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None)
     if st != OK:
         raise FarnError(st, "farn_quant_group")
     return q, scales
+
+
+def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, *, emit_out: bool = True,
+                             residual_out=None, out=None, q=None, scales=None,
+                             variant: int = VARIANT_AUTO, stream=None):
+    """The plain call, then MXFP4 of the bf16 output (OCP MX: 32-channel blocks, E8M0 scales,
+    E2M1 codes two per byte). Returns (residual_out, out or None, q uint8 [T, H/2],
+    scales uint8 [T, H/32])."""
+    p0 = partials[0]
+    T, H = p0.shape
+    dev = p0.device
+    for i, p in enumerate(partials):
+        _check_bf16(f"partials[{i}]", p, (T, H), dev)
+    if residual is not None:
+        _check_bf16("residual", residual, (T, H), dev)
+    _check_bf16("gamma", gamma, (H,), dev)
+    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    if emit_out and out is None:
+        out = torch.empty_like(p0)
+    if not emit_out:
+        out = None
+    q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None else scales
+    if q.dtype != torch.uint8 or q.numel() != T * (H // 2) or not q.is_contiguous():
+        raise ValueError("q: expected contiguous uint8 [T, H/2]")
+    if scales.dtype != torch.uint8 or scales.numel() != T * (H // MX_BLOCK) or not scales.is_contiguous():
+        raise ValueError("scales: expected contiguous uint8 [T, H/32]")
+    st = _lib.farn_reduce_add_rmsnorm_mxfp4_ex(
+        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
+        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
+    if st != OK:
+        raise FarnError(st, "farn_reduce_add_rmsnorm_mxfp4")
+    return residual_out, out, q, scales

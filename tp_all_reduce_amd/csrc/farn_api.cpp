@@ -45,21 +45,25 @@ Range range_of(const void *p, int64_t bytes) {
     return Range{lo, lo + (uintptr_t)bytes};
 }
 
-// Full check of one call. quant = true for the FP8 call.
+// Output quant mode of a fused call.
+enum Quant { kNone = 0, kFp8 = 1, kMxfp4 = 2 };
+
+// Full check of one fused call.
 farn_status check(const void *const *partials, int R, const void *residual, const void *gamma,
-                  float eps, int64_t T, int64_t H, int group_size, bool quant, void *residual_out,
-                  void *out, void *q, float *scales) {
+                  float eps, int64_t T, int64_t H, int group_size, Quant quant, void *residual_out,
+                  void *out, void *q, void *scales) {
     if (R < 1 || R > FARN_MAX_R) return FARN_ERR_SHAPE;
     if (T < 0 || T > ((int64_t)1 << 40) || H <= 0 || H % 8 != 0 || H > FARN_MAX_H)
         return FARN_ERR_SHAPE;
-    if (quant && (group_size != FARN_GROUP || H % FARN_GROUP != 0)) return FARN_ERR_SHAPE;
+    if (quant == kFp8 && (group_size != FARN_GROUP || H % FARN_GROUP != 0)) return FARN_ERR_SHAPE;
+    if (quant == kMxfp4 && H % FARN_MX_BLOCK != 0) return FARN_ERR_SHAPE;
     if (!(eps >= 0.0f) || isinf(eps)) return FARN_ERR_EPS;
     if (!partials || !gamma) return FARN_ERR_NULL;
     if (T == 0) return FARN_OK;  // no row buffer is touched; empty tensors may have NULL data
     for (int r = 0; r < R; ++r)
         if (!partials[r]) return FARN_ERR_NULL;
     if (!residual_out) return FARN_ERR_NULL;
-    if (quant) {
+    if (quant != kNone) {
         if (!q || !scales) return FARN_ERR_NULL;
     } else if (!out) {
         return FARN_ERR_NULL;
@@ -70,7 +74,8 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
         if (!a16(partials[r])) return FARN_ERR_ALIGN;
     if ((residual && !a16(residual)) || !a16(gamma) || !a16(residual_out) || (out && !a16(out)))
         return FARN_ERR_ALIGN;
-    if (quant && (!a16(q) || ((uintptr_t)scales & 3u) != 0)) return FARN_ERR_ALIGN;
+    if (quant != kNone && !a16(q)) return FARN_ERR_ALIGN;
+    if (quant == kFp8 && ((uintptr_t)scales & 3u) != 0) return FARN_ERR_ALIGN;
 
     const int64_t tile = T * H * 2;
     Range ins[FARN_MAX_R + 2];
@@ -83,9 +88,12 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
     int n_out = 0;
     outs[n_out++] = range_of(residual_out, tile);
     if (out) outs[n_out++] = range_of(out, tile);
-    if (quant) {
+    if (quant == kFp8) {
         outs[n_out++] = range_of(q, T * H);
         outs[n_out++] = range_of(scales, T * (H / FARN_GROUP) * 4);
+    } else if (quant == kMxfp4) {
+        outs[n_out++] = range_of(q, T * H / 2);
+        outs[n_out++] = range_of(scales, T * (H / FARN_MX_BLOCK));
     }
     for (int i = 0; i < n_out; ++i) {
         for (int j = 0; j < n_in; ++j)
@@ -119,13 +127,13 @@ int select(int R, int64_t T, int64_t H, int quant) {
 }
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
-                float eps, int64_t T, int64_t H, int group_size, bool quant, void *residual_out,
-                void *out, void *q, float *scales, void *stream, int variant) {
+                float eps, int64_t T, int64_t H, int group_size, Quant quant, void *residual_out,
+                void *out, void *q, void *scales, void *stream, int variant) {
     if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH) return FARN_ERR_VARIANT;
     farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
                            residual_out, out, q, scales);
     if (st != FARN_OK || T == 0) return st;
-    if (variant == FARN_VARIANT_AUTO) variant = select(R, T, H, quant ? 1 : 0);
+    if (variant == FARN_VARIANT_AUTO) variant = select(R, T, H, quant != kNone ? 1 : 0);
     if (T > INT32_MAX) return FARN_ERR_SHAPE;  // one workgroup per row
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
@@ -137,8 +145,9 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     c.H = H;
     c.residual_out = residual_out;
     c.out = out;
-    c.q = quant ? q : nullptr;
-    c.scales = quant ? scales : nullptr;
+    c.q = quant != kNone ? q : nullptr;
+    c.scales = quant != kNone ? scales : nullptr;
+    c.mxfp4 = quant == kMxfp4;
     c.stream = stream;
     return farn::launch(c, variant) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
@@ -231,7 +240,7 @@ farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size
 farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,
                                     const void *gamma, float eps, int64_t T, int64_t H,
                                     void *residual_out, void *out, void *stream) {
-    return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
+    return run(partials, R, residual, gamma, eps, T, H, 0, kNone, residual_out, out, nullptr,
                nullptr, stream, FARN_VARIANT_AUTO);
 }
 
@@ -240,14 +249,14 @@ farn_status farn_reduce_add_rmsnorm_quant_group(const void *const *partials, int
                                                 int64_t T, int64_t H, int group_size,
                                                 void *residual_out, void *out, void *q,
                                                 float *scales, void *stream) {
-    return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
+    return run(partials, R, residual, gamma, eps, T, H, group_size, kFp8, residual_out, out, q,
                scales, stream, FARN_VARIANT_AUTO);
 }
 
 farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
                                        const void *gamma, float eps, int64_t T, int64_t H,
                                        void *residual_out, void *out, void *stream, int variant) {
-    return run(partials, R, residual, gamma, eps, T, H, 0, false, residual_out, out, nullptr,
+    return run(partials, R, residual, gamma, eps, T, H, 0, kNone, residual_out, out, nullptr,
                nullptr, stream, variant);
 }
 
@@ -256,8 +265,24 @@ farn_status farn_reduce_add_rmsnorm_quant_group_ex(const void *const *partials, 
                                                    float eps, int64_t T, int64_t H, int group_size,
                                                    void *residual_out, void *out, void *q,
                                                    float *scales, void *stream, int variant) {
-    return run(partials, R, residual, gamma, eps, T, H, group_size, true, residual_out, out, q,
+    return run(partials, R, residual, gamma, eps, T, H, group_size, kFp8, residual_out, out, q,
                scales, stream, variant);
+}
+
+farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, const void *residual,
+                                          const void *gamma, float eps, int64_t T, int64_t H,
+                                          void *residual_out, void *out, void *q, void *scales,
+                                          void *stream) {
+    return run(partials, R, residual, gamma, eps, T, H, 0, kMxfp4, residual_out, out, q, scales,
+               stream, FARN_VARIANT_AUTO);
+}
+
+farn_status farn_reduce_add_rmsnorm_mxfp4_ex(const void *const *partials, int R, const void *residual,
+                                             const void *gamma, float eps, int64_t T, int64_t H,
+                                             void *residual_out, void *out, void *q, void *scales,
+                                             void *stream, int variant) {
+    return run(partials, R, residual, gamma, eps, T, H, 0, kMxfp4, residual_out, out, q, scales,
+               stream, variant);
 }
 
 int farn_select_variant(int R, int64_t T, int64_t H, int quant) { return select(R, T, H, quant); }

@@ -20,8 +20,9 @@ struct Call {
     int64_t T, H;
     void *residual_out;
     void *out;     // null only for the quant call with the bf16 output off
-    void *q;       // quant call only
-    float *scales; // quant call only
+    void *q;       // quant calls only
+    void *scales;  // quant calls only (fp32 for FP8, E8M0 bytes for MXFP4)
+    bool mxfp4 = false;  // q / scales hold MXFP4 (else FP8 group-128)
     const void *x = nullptr;  // kQuant input
     void *stream;
 };

@@ -52,8 +52,8 @@ struct Params {
     const void *gamma;  // [H]
     void *res_out;
     void *out;          // null: bf16 output not written (quant call only)
-    void *q;            // E4M3 codes [T,H] (quant only)
-    float *scales;      // [T, H/128] (quant only)
+    void *q;            // E4M3 codes [T,H] (FP8), or E2M1 code pairs [T,H/2] (MXFP4)
+    void *scales;       // fp32 [T, H/128] (FP8), or E8M0 bytes [T, H/32] (MXFP4)
     const void *x;      // bf16 [T,H] input of the standalone quant kernel
     int64_t T;
     int nvec;           // H / 8
@@ -63,6 +63,11 @@ struct Params {
 };
 
 constexpr int kMaxWaves = 16;
+
+// Output quant modes of the fused kernel.
+constexpr int kQuantNone = 0;   // bf16 out only
+constexpr int kQuantFp8 = 1;    // + E4M3 codes and fp32 scales per 128 channels
+constexpr int kQuantMxfp4 = 2;  // + E2M1 code pairs and E8M0 scales per 32 channels
 
 // ---------------------------------------------------------------- buffer access
 // Every global access goes through a buffer resource covering exactly one row of one
@@ -97,6 +102,12 @@ __device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void st4(float v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kStoreCodePolicy);
+}
+__device__ __forceinline__ void st4u(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStoreCodePolicy);
+}
+__device__ __forceinline__ void st1(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, kStoreCodePolicy);
 }
 
 // ---------------------------------------------------------------- number formats
@@ -160,6 +171,23 @@ __device__ __forceinline__ uint32_t e4m3_code(float o, float scale, float inv) {
     return s | c;
 }
 
+// FP4 E2M1 code (OCP Microscaling Formats (MX) v1.0: 1 sign, 2 exponent bits with
+// bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) of x, which is exact
+// (a bf16 value times a power of two), rounded once to nearest even, magnitudes above 6
+// clamped to 6. The grid step is 0.5 below 2, 1 in [2, 4) and 2 in [4, 8); on each
+// piece the code is an offset plus rint(x / step), and ties to an even multiple of the
+// step are ties to the even code.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+    const uint32_t s = (__float_as_uint(x) >> 28) & 0x8u;
+    const float a = __builtin_fabsf(x);
+    const float c0 = __builtin_rintf(a * 2.0f);          // codes 0..4 for a < 2
+    const float c1 = __builtin_rintf(a) + 2.0f;          // codes 4..6 for 2 <= a < 4
+    const float c2 = __builtin_rintf(a * 0.5f) + 4.0f;   // codes 6..8 for 4 <= a < 8
+    float c = a < 2.0f ? c0 : (a < 4.0f ? c1 : c2);
+    c = a >= 6.0f ? 7.0f : c;
+    return s | (uint32_t)c;
+}
+
 // ---------------------------------------------------------------- cross-lane
 // DPP controls (gfx9): quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E,
 // row_half_mirror = 0x141, row_mirror = 0x140. After the four steps every lane of a
@@ -202,6 +230,13 @@ __device__ __forceinline__ double readlane_d(double x, int lane) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Max over the 4 lanes of a quad (one 32-channel MXFP4 block: 4 lanes x 8 values).
+__device__ __forceinline__ uint32_t quad_umax(uint32_t x) {
+    x = max(x, dpp_u<0xB1>(x));
+    x = max(x, dpp_u<0x4E>(x));
+    return x;
 }
 
 // Wave total: the four 16-lane row totals, read as scalars and added in a fixed order.
@@ -309,9 +344,32 @@ __device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc
     st4(scale, r_sc, soff);
 }
 
+// MXFP4 of one vector slot: the 32-channel block spans the 4 lanes of a quad. Shared
+// scale 2^s with s = floor(log2 amax) - 2 (E2M1's largest exponent), clamped to the
+// E8M0 range; a block holding a NaN gets the NaN scale 0xFF and zero codes, an all-zero
+// block scale 2^-127 (byte 0) and zero codes. Element 2i goes to the low nibble.
+__device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
+    uint32_t amax = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
+    amax = quad_umax(amax);
+    const bool nan_blk = amax > 0x7f800000u;
+    const bool zero_blk = amax == 0u;
+    int sexp = __builtin_amdgcn_frexp_expf(__uint_as_float(amax)) - 1 - 2;  // floor(log2 amax) - 2
+    sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
+    const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) word |= e2m1_code(__builtin_ldexpf(o[e], -sexp)) << (4 * e);
+    st4u(word & keep, r_q, off >> 2);
+    const uint32_t sbyte = nan_blk ? 0xffu : (zero_blk ? 0u : (uint32_t)(sexp + 127));
+    // one lane per quad writes the scale byte; the others aim past the row (dropped)
+    st1(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
+}
+
 // Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16), store
-// out, and (QUANT) its E4M3 codes and group scale.
-template <bool QUANT>
+// out, and (QM) its quantised codes and scales.
+template <int QM>
 __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out,
                                            rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
     float o[8];
@@ -325,14 +383,15 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
         o[2 * w + 1] = bf_hi(packed[w]);
     }
     st16(packed, r_out, off);
-    if constexpr (QUANT) quant_slot(o, r_q, r_sc, off);
+    if constexpr (QM == kQuantFp8) quant_slot(o, r_q, r_sc, off);
+    if constexpr (QM == kQuantMxfp4) mxfp4_slot(o, r_q, r_sc, off);
 }
 
 // Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
 // lane the second slot's loads are issued before the first is reduced; with four (rows
 // beyond 16384 channels) the slots are loaded and reduced one after the other, to bound
 // register use.
-template <int R, int VPL, bool QUANT>
+template <int R, int VPL, int QM>
 __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
                                        const Params &k, int64_t t, double *slot) {
     const uint32_t L16 = blockDim.x * 16u;
@@ -358,11 +417,13 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     }
     const double rstd = row_rstd(ss, k, slot);
     const rsrc_t r_out = row_rsrc(k.out, k.out ? ro : 0, k.out ? rb : 0);
-    const rsrc_t r_q = row_rsrc(k.q, QUANT ? t * (int64_t)k.nvec * 8 : 0, QUANT ? k.nvec * 8 : 0);
-    const rsrc_t r_sc = row_rsrc(k.scales, QUANT ? t * (int64_t)k.ngroups * 4 : 0,
-                                 QUANT ? k.ngroups * 4 : 0);
+    // per-row code and scale bytes: FP8 H and 4*H/128; MXFP4 H/2 and H/32
+    const int qb = QM == kQuantFp8 ? k.nvec * 8 : (QM == kQuantMxfp4 ? k.nvec * 4 : 0);
+    const int sb = QM == kQuantFp8 ? k.ngroups * 4 : (QM == kQuantMxfp4 ? k.nvec / 4 : 0);
+    const rsrc_t r_q = row_rsrc(k.q, t * (int64_t)qb, qb);
+    const rsrc_t r_sc = row_rsrc(k.scales, t * (int64_t)sb, sb);
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) store_slot<QUANT>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16);
+    for (int v = 0; v < VPL; ++v) store_slot<QM>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16);
 }
 
 template <int VPL>
@@ -373,7 +434,7 @@ __device__ __forceinline__ void load_gamma(u32x4 (&gam)[VPL], const Params &k) {
 }
 
 // ---------------------------------------------------------------- kernels
-template <int R, int VPL, bool QUANT>
+template <int R, int VPL, int QM>
 __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     __shared__ double slot[kMaxWaves];
     const int64_t t = blockIdx.x;
@@ -381,7 +442,7 @@ __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     load_slot<R>(in, k, t, threadIdx.x * 16u);
     u32x4 gam[VPL];
     load_gamma<VPL>(gam, k);
-    do_row<R, VPL, QUANT>(in, gam, k, t, slot);
+    do_row<R, VPL, QM>(in, gam, k, t, slot);
 }
 
 // Unfused building blocks (the compositions the fused call replaces): the all-reduce
@@ -408,7 +469,7 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
     const rsrc_t r_x = row_rsrc(k.x, t * (int64_t)rb, rb);
     const rsrc_t r_q = row_rsrc(k.q, t * (int64_t)k.nvec * 8, k.nvec * 8);
     const rsrc_t r_sc = row_rsrc(k.scales, t * (int64_t)k.ngroups * 4, k.ngroups * 4);
-    u32x4 xv[VPL];
+    u32x4 xv[VPL];  // (the standalone quant is the FP8 group quant)
 #pragma unroll
     for (int v = 0; v < VPL; ++v) xv[v] = ld16(r_x, (v * blockDim.x + threadIdx.x) * 16u);
 #pragma unroll
@@ -426,9 +487,9 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
 // ---------------------------------------------------------------- dispatch tables
 typedef void (*KernelFn)(const Params);
 
-template <int R, bool Q>
+template <int R, int QM>
 struct Row {
-    static constexpr KernelFn fn[3] = {farn_rows<R, 1, Q>, farn_rows<R, 2, Q>, farn_rows<R, 4, Q>};
+    static constexpr KernelFn fn[3] = {farn_rows<R, 1, QM>, farn_rows<R, 2, QM>, farn_rows<R, 4, QM>};
 };
 
 template <int R>
@@ -449,11 +510,11 @@ KernelFn pick_reduce(int R, int vi) {
     }
 }
 
-template <bool Q>
+template <int QM>
 KernelFn pick(int R, int vi) {
     switch (R) {
 #define FARN_CASE(n) \
-    case n: return Row<n, Q>::fn[vi];
+    case n: return Row<n, QM>::fn[vi];
         FARN_CASE(1) FARN_CASE(2) FARN_CASE(3) FARN_CASE(4)
         FARN_CASE(5) FARN_CASE(6) FARN_CASE(7) FARN_CASE(8)
 #undef FARN_CASE
@@ -474,7 +535,8 @@ int launch(const Call &c, int variant) {
     } else if (c.kind == Kind::kQuant) {
         fn = kQuantRows[vi];
     } else {
-        fn = c.q != nullptr ? pick<true>(c.R, vi) : pick<false>(c.R, vi);
+        fn = c.q == nullptr ? pick<kQuantNone>(c.R, vi)
+                            : (c.mxfp4 ? pick<kQuantMxfp4>(c.R, vi) : pick<kQuantFp8>(c.R, vi));
     }
     if (!fn) return 1;
 
