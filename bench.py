@@ -44,6 +44,8 @@ WORKLOADS = {
     "decode_ds": (CONFIGS["decode_ds"], False, True),
     "decode_fp8": (CONFIGS["decode_fp8"], True, True),
     "tiny": (CONFIGS["tiny"], False, True),
+    "prefill_mxfp4": (CONFIGS["prefill"], "mxfp4", True),
+    "decode_ds_mxfp4": (CONFIGS["decode_ds"], "mxfp4", True),
 }
 for _T in (2 ** k for k in range(1, 13)):
     WORKLOADS[f"sweep_T{_T}"] = (sweep_config(_T), False, True)
@@ -60,7 +62,8 @@ def kernel_hash() -> str:
 
 
 def describe(cfg, quant, emit_out):
-    q = ", FP8 group-128 quant" + (" + bf16 out" if emit_out else ", bf16 out not written") if quant else ""
+    kind = ", MXFP4 (32-channel E8M0 blocks)" if quant == "mxfp4" else ", FP8 group-128 quant"
+    q = kind + (" + bf16 out" if emit_out else ", bf16 out not written") if quant else ""
     return f"{cfg.what}: R={cfg.R} T={cfg.T} H={cfg.H}{q}"
 
 
@@ -80,8 +83,12 @@ class Bufs:
         T, H = self.T, self.H
         self.ro = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if (self.emit_out or not self.quant) else None
-        self.q = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.quant else None
-        self.s = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.quant else None
+        if self.quant == "mxfp4":
+            self.q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+            self.s = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        else:
+            self.q = torch.empty((T, H), dtype=torch.uint8, device=dev) if self.quant else None
+            self.s = torch.empty((T, H // 128), dtype=torch.float32, device=dev) if self.quant else None
 
     def clone(self, dev):
         c = object.__new__(Bufs)
@@ -107,7 +114,11 @@ class Bufs:
         F.quant_group(self.out, q=self.q, scales=self.s)
 
     def call(self, variant):
-        if self.quant:
+        if self.quant == "mxfp4":
+            F.reduce_add_rmsnorm_mxfp4(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
+                                       residual_out=self.ro, out=self.out, q=self.q, scales=self.s,
+                                       variant=variant)
+        elif self.quant:
             F.reduce_add_rmsnorm_quant_group(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
                                              residual_out=self.ro, out=self.out, q=self.q, scales=self.s,
                                              variant=variant)
@@ -117,6 +128,9 @@ class Bufs:
 
 
 def nbytes(cfg, quant, emit_out):
+    if quant == "mxfp4":
+        th = cfg.T * cfg.H
+        return cfg.nbytes_plain + th // 2 + th // 32 - (0 if emit_out else th * 2)
     return cfg.nbytes_quant(emit_out) if quant else cfg.nbytes_plain
 
 
@@ -166,7 +180,12 @@ def parity_gate(d, bufs, quant, emit_out, rows):
     from tests.parity import compare_bf16, compare_fp8, from_dev_bf16, within_tolerance
     P = d["partials"][:, rows, :]
     res = d["residual"][rows]
-    if quant:
+    if quant == "mxfp4":
+        from tests.parity import compare_mxfp4, mxfp4_within_tolerance
+        r_ro, r_out, r_q, r_s = oracle.reduce_add_rmsnorm_mxfp4(P, res, d["gamma"], 1e-6, emit_out, nthreads=8)
+        mx = compare_mxfp4(bufs.q.cpu().numpy()[rows], r_q, bufs.s.cpu().numpy()[rows], r_s)
+        fp8 = None
+    elif quant:
         r_ro, r_out, r_q, r_s = oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], 1e-6, 128,
                                                                       emit_out, nthreads=8)
         fp8 = compare_fp8(bufs.q.cpu().numpy()[rows], r_q, bufs.s.cpu().numpy()[rows], r_s)
@@ -176,6 +195,9 @@ def parity_gate(d, bufs, quant, emit_out, rows):
     rep_ro = compare_bf16("residual_out", from_dev_bf16(bufs.ro)[rows], r_ro)
     rep_out = compare_bf16("out", from_dev_bf16(bufs.out)[rows], r_out) if bufs.out is not None else None
     ok, why = within_tolerance(rep_ro, rep_out, fp8)
+    if quant == "mxfp4":
+        ok2, why2 = mxfp4_within_tolerance(mx)
+        ok, why = ok and ok2, "; ".join(w for w in (why, why2) if w)
     return {"ok": ok, "why": why, "rows_checked": int(len(rows)),
             "residual_out_bit_diffs": rep_ro["n_bit_diff"],
             "out_max_rel_err": None if rep_out is None else rep_out["max_rel_err"],
@@ -192,7 +214,10 @@ def cpu_baseline(d, cfg, quant, emit_out, budget_s):
     passes, spent = 0, 0.0
     while spent < budget_s:
         t0 = time.perf_counter()
-        if quant:
+        if quant == "mxfp4":
+            oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], 1e-6, emit_out,
+                                            nthreads=threads)
+        elif quant:
             oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], 1e-6, 128,
                                                   emit_out, nthreads=threads)
         else:
@@ -240,12 +265,18 @@ def secondary(dev, steps):
                      "bytes_per_call": nb}
         del sets, b
         torch.cuda.empty_cache()
-    cfg, quant, emit = WORKLOADS["prefill"]
+    for name in ("prefill", "prefill_mxfp4"):
+        cfg, quant, emit = WORKLOADS[name]
+        b = Bufs(make_inputs(cfg), dev, quant, emit)
+        nb = nbytes(cfg, quant, emit)
+        ms, _ = time_calls([b], F.VARIANT_AUTO, 50, 20)
+        out[name] = {"us_per_call": round(ms * 1e3, 2), "GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "bytes_per_call": nb}
+        del b
+        torch.cuda.empty_cache()
+    cfg, quant, emit = WORKLOADS["decode_ds_mxfp4"]
     b = Bufs(make_inputs(cfg), dev, quant, emit)
-    ms, _ = time_calls([b], F.VARIANT_AUTO, 50, 5)
-    out["prefill"] = {"us_per_call": round(ms * 1e3, 2),
-                      "GBps": round(cfg.nbytes_plain / (ms * 1e-3) / 1e9, 1),
-                      "bytes_per_call": cfg.nbytes_plain}
+    out["decode_ds_mxfp4"] = {"us_per_call_graph_hot": round(time_graph([b], F.VARIANT_AUTO, 200, 10) * 1e3, 2)}
     return out
 
 

@@ -63,7 +63,8 @@ typedef enum farn_status {
                              overlap: residual_out == residual exactly, in place) */
     FARN_ERR_EPS = 5,     /* eps is not finite or is negative */
     FARN_ERR_LAUNCH = 6,  /* the kernel launch failed */
-    FARN_ERR_VARIANT = 7  /* unknown variant in an _ex call */
+    FARN_ERR_VARIANT = 7  /* unknown variant or option bit in an _ex call, or column-major
+                             scales asked of a call without FP8 scales */
 } farn_status;
 
 /* Largest TP degree the pages run is 8 ("[AMD] Support --enable-aiter-allreduce-fusion
@@ -137,7 +138,15 @@ typedef enum farn_variant {
     FARN_VARIANT_BANDWIDTH = 2
 } farn_variant;
 
-/* As the calls above, with the launch shape forced. For tests and the bench. */
+/* Option bit of the _ex calls, or-ed into `variant`: FP8 scales laid out column-major,
+   scales[g * T + t] for group g of row t ([H/128, T], the transposed per-token-group
+   layout FP8 GEMMs read; the sglang #24651 summary's consumers take (fp8, scale) pairs
+   and its related-PR notes mention scale layout utilities for AMD FP8). Requires
+   T * H/128 * 4 < 2^31 bytes. */
+#define FARN_SCALES_COL_MAJOR 0x100
+
+/* As the calls above, with the launch shape forced (variant: a farn_variant, or-ed with
+   option bits). For tests, the bench and callers that need an option. */
 farn_status farn_reduce_add_rmsnorm_ex(const void *const *partials, int R, const void *residual,
                                        const void *gamma, float eps, int64_t T, int64_t H,
                                        void *residual_out, void *out, void *stream, int variant);

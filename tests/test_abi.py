@@ -229,3 +229,15 @@ def test_mxfp4_rejections(what, fn, want):
 
 def test_mxfp4_accepts_byte_aligned_scales_and_null_out():
     assert mx_call(T=0, scales=0x10_4000_0001, out=0) == OK
+
+
+def test_option_bits():
+    c = FakeCall(quant=True)
+    c.variant = 0x100 | 1
+    c.T = 0
+    assert c.call() == OK
+    c.variant = 0x200
+    assert c.call() == VARIANT
+    p = FakeCall()
+    p.variant = 0x100  # column-major scales asked of the plain call
+    assert p.call() == VARIANT

@@ -424,3 +424,35 @@ def test_mxfp4_no_residual_no_out_and_special_blocks(dev):
     scn = sc.cpu().numpy()
     assert scn[1, 1] == 0 and np.all(q.cpu().numpy()[1, 16:32] == 0)
     assert np.all(scn[2] == 0xFF)  # the NaN makes the whole row's out NaN
+
+
+@pytest.mark.parametrize("name", ["decode_ds", "decode_fp8"])
+def test_fp8_scales_column_major(dev, name):
+    """Column-major scales ([H/128, T]) hold the same values as the row-major ones, transposed;
+    codes and bf16 outputs are unchanged."""
+    u = Uploaded(make_inputs(CONFIGS[name], seed=95), dev)
+    say(f"[gpu] column-major scales {name}")
+    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+        a = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant)
+        b = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant, scales_col_major=True)
+        torch.cuda.synchronize()
+        for x, y in zip(a[:3], b[:3]):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+        assert b[3].shape == (u.H // 128, u.T) and torch.equal(a[3].t().contiguous(), b[3])
+
+
+def test_random_shapes(dev):
+    """Seeded random shapes through every entry point and both launch shapes."""
+    rng = np.random.default_rng(2024)
+    for i in range(24):
+        R = int(rng.integers(1, 9))
+        T = int(rng.integers(1, 300))
+        H = int(rng.integers(1, 129)) * 128 if i % 3 else int(rng.integers(1, 2049)) * 8
+        d = make_inputs(CONFIGS["decode_fp8"], seed=1000 + i, R=R, T=T, H=H)
+        u = Uploaded(d, dev, residual=bool(i % 4))
+        variant = ["auto", "latency", "bandwidth"][i % 3]
+        run_and_compare(u, False, variant, label=f"rand{i}")
+        if H % 128 == 0:
+            run_and_compare(u, True, variant, emit_out=bool(i % 2), label=f"rand{i}")
+        if H % 32 == 0:
+            run_mxfp4(u, variant, emit_out=bool(i % 2), label=f"rand{i}")

@@ -25,6 +25,7 @@ OK = 0
 STATUS = {0: "FARN_OK", 1: "FARN_ERR_NULL", 2: "FARN_ERR_SHAPE", 3: "FARN_ERR_ALIGN",
           4: "FARN_ERR_ALIAS", 5: "FARN_ERR_EPS", 6: "FARN_ERR_LAUNCH", 7: "FARN_ERR_VARIANT"}
 VARIANT_AUTO, VARIANT_LATENCY, VARIANT_BANDWIDTH = 0, 1, 2
+SCALES_COL_MAJOR = 0x100
 MAX_R, MAX_H, GROUP, MX_BLOCK = 8, 32768, 128, 32
 EXPORTS = ("farn_reduce_add_rmsnorm", "farn_reduce_add_rmsnorm_quant_group",
            "farn_reduce_add_rmsnorm_ex", "farn_reduce_add_rmsnorm_quant_group_ex",
@@ -132,9 +133,10 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
 def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6, *,
                                    group_size: int = GROUP, emit_out: bool = True, residual_out=None,
                                    out=None, q=None, scales=None, variant: int = VARIANT_AUTO,
-                                   stream=None):
+                                   scales_col_major: bool = False, stream=None):
     """The plain call, then per-128-channel E4M3 quant of the bf16 output. Returns
-    (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128])."""
+    (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128], or
+    [H/128, T] with scales_col_major)."""
     p0 = partials[0]
     T, H = p0.shape
     dev = p0.device
@@ -150,14 +152,16 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
         out = None
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
     G = H // group_size if group_size > 0 else 0
-    scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
+    if scales is None:
+        scales = torch.empty((G, T) if scales_col_major else (T, G), dtype=torch.float32, device=dev)
     if q.dtype not in (torch.uint8, torch.float8_e4m3fn) or q.numel() != T * H or not q.is_contiguous():
         raise ValueError("q: expected contiguous uint8 / float8_e4m3fn [T, H]")
     if scales.dtype != torch.float32 or scales.numel() != T * G or not scales.is_contiguous():
         raise ValueError("scales: expected contiguous float32 [T, H/group_size]")
     st = _lib.farn_reduce_add_rmsnorm_quant_group_ex(
         _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
-        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
+        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream),
+        variant | (SCALES_COL_MAJOR if scales_col_major else 0))
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
     return residual_out, out, q, scales

@@ -128,12 +128,18 @@ int select(int R, int64_t T, int64_t H, int quant) {
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
                 float eps, int64_t T, int64_t H, int group_size, Quant quant, void *residual_out,
-                void *out, void *q, void *scales, void *stream, int variant) {
+                void *out, void *q, void *scales, void *stream, int options) {
+    const int variant = options & 0xff;
+    const bool cols = (options & FARN_SCALES_COL_MAJOR) != 0;
+    if ((options & ~(0xff | FARN_SCALES_COL_MAJOR)) != 0) return FARN_ERR_VARIANT;
     if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH) return FARN_ERR_VARIANT;
+    if (cols && quant != kFp8) return FARN_ERR_VARIANT;
+    // column-major scales are addressed through one 32-bit buffer range
+    if (cols && T * (H / FARN_GROUP) * 4 >= ((int64_t)1 << 31)) return FARN_ERR_SHAPE;
     farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
                            residual_out, out, q, scales);
     if (st != FARN_OK || T == 0) return st;
-    if (variant == FARN_VARIANT_AUTO) variant = select(R, T, H, quant != kNone ? 1 : 0);
+    const int shape = variant == FARN_VARIANT_AUTO ? select(R, T, H, quant != kNone ? 1 : 0) : variant;
     if (T > INT32_MAX) return FARN_ERR_SHAPE;  // one workgroup per row
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
@@ -148,8 +154,9 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     c.q = quant != kNone ? q : nullptr;
     c.scales = quant != kNone ? scales : nullptr;
     c.mxfp4 = quant == kMxfp4;
+    c.scale_cols = cols;
     c.stream = stream;
-    return farn::launch(c, variant) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, shape) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 // Checks of the standalone all-reduce: partials -> out.
@@ -296,7 +303,7 @@ const char *farn_status_string(int status) {
         case FARN_ERR_ALIAS: return "an output overlaps an input or another output";
         case FARN_ERR_EPS: return "eps is not finite or is negative";
         case FARN_ERR_LAUNCH: return "kernel launch failed";
-        case FARN_ERR_VARIANT: return "unknown variant";
+        case FARN_ERR_VARIANT: return "unknown variant or option";
         default: return "unknown status";
     }
 }

@@ -22,7 +22,8 @@ struct Call {
     void *out;     // null only for the quant call with the bf16 output off
     void *q;       // quant calls only
     void *scales;  // quant calls only (fp32 for FP8, E8M0 bytes for MXFP4)
-    bool mxfp4 = false;  // q / scales hold MXFP4 (else FP8 group-128)
+    bool mxfp4 = false;       // q / scales hold MXFP4 (else FP8 group-128)
+    bool scale_cols = false;  // FP8 scales column-major [H/128, T]
     const void *x = nullptr;  // kQuant input
     void *stream;
 };

@@ -55,6 +55,7 @@ struct Params {
     void *q;            // E4M3 codes [T,H] (FP8), or E2M1 code pairs [T,H/2] (MXFP4)
     void *scales;       // fp32 [T, H/128] (FP8), or E8M0 bytes [T, H/32] (MXFP4)
     const void *x;      // bf16 [T,H] input of the standalone quant kernel
+    int scale_cols;     // FP8 scales column-major [H/128, T] (else row-major [T, H/128])
     int64_t T;
     int nvec;           // H / 8
     int ngroups;        // H / 128
@@ -321,8 +322,9 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
 }
 
 // E4M3 codes of one vector slot (8 bf16 values as floats) and, from one lane per
-// 16-lane group, the group's scale.
-__device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
+// 16-lane group, the group's scale, stored at byte sbase + group * sstride of r_sc.
+__device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off,
+                                           uint32_t sbase, uint32_t sstride) {
     uint32_t amax = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
@@ -340,7 +342,7 @@ __device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc
     codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     st8(codes, r_q, off >> 1);
     // one lane per group writes the scale; the others aim past the row (dropped)
-    const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? (off >> 8) * 4u : kDropOffset;
+    const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off >> 8) * sstride : kDropOffset;
     st4(scale, r_sc, soff);
 }
 
@@ -371,7 +373,8 @@ __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc
 // out, and (QM) its quantised codes and scales.
 template <int QM>
 __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out,
-                                           rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
+                                           rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
+                                           uint32_t sstride) {
     float o[8];
     u32x4 packed;
 #pragma unroll
@@ -383,7 +386,7 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
         o[2 * w + 1] = bf_hi(packed[w]);
     }
     st16(packed, r_out, off);
-    if constexpr (QM == kQuantFp8) quant_slot(o, r_q, r_sc, off);
+    if constexpr (QM == kQuantFp8) quant_slot(o, r_q, r_sc, off, sbase, sstride);
     if constexpr (QM == kQuantMxfp4) mxfp4_slot(o, r_q, r_sc, off);
 }
 
@@ -421,9 +424,16 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const int qb = QM == kQuantFp8 ? k.nvec * 8 : (QM == kQuantMxfp4 ? k.nvec * 4 : 0);
     const int sb = QM == kQuantFp8 ? k.ngroups * 4 : (QM == kQuantMxfp4 ? k.nvec / 4 : 0);
     const rsrc_t r_q = row_rsrc(k.q, t * (int64_t)qb, qb);
-    const rsrc_t r_sc = row_rsrc(k.scales, t * (int64_t)sb, sb);
+    // FP8 scales row-major: this row's H/128 floats; column-major: the whole [H/128, T]
+    // array (the host keeps it under 2^31 bytes), row t's scale of group g at (g*T + t)*4
+    const bool cols = QM == kQuantFp8 && k.scale_cols;
+    const rsrc_t r_sc = cols ? row_rsrc(k.scales, 0, (int)(k.T * k.ngroups * 4))
+                             : row_rsrc(k.scales, t * (int64_t)sb, sb);
+    const uint32_t sbase = cols ? (uint32_t)t * 4u : 0u;
+    const uint32_t sstride = cols ? (uint32_t)k.T * 4u : 4u;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) store_slot<QM>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16);
+    for (int v = 0; v < VPL; ++v)
+        store_slot<QM>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16, sbase, sstride);
 }
 
 template <int VPL>
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
             o[2 * w] = bf_lo(xv[v][w]);
             o[2 * w + 1] = bf_hi(xv[v][w]);
         }
-        quant_slot(o, r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u);
+        quant_slot(o, r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
     }
 }
 
@@ -549,6 +559,7 @@ int launch(const Call &c, int variant) {
     k.q = c.q;
     k.scales = c.scales;
     k.x = c.x;
+    k.scale_cols = c.scale_cols ? 1 : 0;
     k.T = c.T;
     k.nvec = (int)(c.H / 8);
     k.ngroups = (int)(c.H / 128);
