@@ -241,3 +241,11 @@ def test_option_bits():
     p = FakeCall()
     p.variant = 0x100  # column-major scales asked of the plain call
     assert p.call() == VARIANT
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU; asked for more it exits with a message before touching a GPU."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([os.sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                          capture_output=True, text=True, timeout=300)
+    assert proc.returncode == 2 and "one GPU" in proc.stderr
