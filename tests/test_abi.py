@@ -249,3 +249,17 @@ def test_bench_refuses_several_gpus():
     proc = subprocess.run([os.sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                           capture_output=True, text=True, timeout=300)
     assert proc.returncode == 2 and "one GPU" in proc.stderr
+
+
+def test_c_client_builds_against_header_alone(tmp_path):
+    """A C program (not C++) that includes only include/farn.h and the HIP runtime API
+    compiles warning-free with gcc and links against libfarn.so: the header is valid C."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    exe = str(tmp_path / "client")
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic-errors",
+                    "-Wno-error=pedantic", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+                    os.path.join(root, "tests", "c_abi_client.c"), "-o", exe,
+                    f"-L{os.path.dirname(F.LIB_PATH)}", "-lfarn", f"-L{rocm}/lib", "-lamdhip64"],
+                   check=True)
+    assert os.path.getsize(exe) > 0

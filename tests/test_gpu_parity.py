@@ -456,3 +456,17 @@ def test_random_shapes(dev):
             run_and_compare(u, True, variant, emit_out=bool(i % 2), label=f"rand{i}")
         if H % 32 == 0:
             run_mxfp4(u, variant, emit_out=bool(i % 2), label=f"rand{i}")
+
+
+def test_plain_c_client():
+    """tests/c_abi_client.c: a C program with no Python and no torch calls the ABI on
+    hipMalloc'd memory and checks closed-form results (exit status 0 = all hold)."""
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_client")
+    if not os.path.exists(exe):
+        pytest.fail("tests/c_abi_client is not built (python tp_all_reduce_amd/build.py builds it)")
+    print("case: plain C client", flush=True)
+    proc = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert proc.returncode == 0, proc.stdout + proc.stderr
+    assert "0 mismatches" in proc.stdout

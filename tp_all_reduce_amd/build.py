@@ -5,7 +5,9 @@
 (Run it by path: importing the package loads the built library.)
 
 The C-ABI layer (csrc/farn_api.cpp) makes no HIP call and is compiled by g++; the
-kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two.
+kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two. The plain C
+client of the ABI that the GPU tests run (tests/c_abi_client.c) is compiled by gcc
+against include/farn.h and the built library.
 """
 
 from __future__ import annotations
@@ -19,6 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfarn.so")
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_abi_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -51,10 +56,23 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + f".tmp{os.getpid()}"
     out += _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o])
     os.replace(tmp, LIB)
+    out += build_c_client()
     if verbose:
         for ln in out:
             print(ln)
     return LIB
+
+
+def build_c_client() -> list:
+    """gcc, no HIP compiler: the client sees only the C header, the HIP runtime API and
+    libfarn.so (found next to the package through the rpath)."""
+    tmp = C_CLIENT + f".tmp{os.getpid()}"
+    out = _run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                f"-I{ROCM}/include", C_CLIENT_SRC, "-o", tmp, f"-L{HERE}", "-lfarn",
+                f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../tp_all_reduce_amd",
+                f"-Wl,-rpath,{ROCM}/lib"])
+    os.replace(tmp, C_CLIENT)
+    return out
 
 
 if __name__ == "__main__":
