@@ -262,6 +262,45 @@ def test_subnormal_and_tiny_values(dev):
         run_and_compare(u, True, variant, label="subnormal")
 
 
+def _with_group_exponents(x, exps, rng):
+    """bf16 array x [.., H]: channel group g (128 channels) gets biased exponent exps[g]
+    (0 = subnormal, with a nonzero mantissa), random sign and mantissa."""
+    x = x.astype(np.uint32).copy()
+    for gi, e in enumerate(exps):
+        sl = (..., slice(gi * 128, (gi + 1) * 128))
+        mant = rng.integers(1 if e == 0 else 0, 128, size=x[sl].shape, dtype=np.uint32)
+        sign = rng.integers(0, 2, size=x[sl].shape, dtype=np.uint32) << 15
+        x[sl] = sign | (np.uint32(e) << 7) | mant
+    return x.astype(np.uint16)
+
+
+# per-group exponents of gamma (or x): a normal group; groups whose scale lands on either
+# side of 2^-64; groups whose scale is an fp32 subnormal (1/scale overflows fp32); bf16
+# subnormal values
+TINY_GROUP_EXPONENTS = [127, 70, 69, 27, 4, 1, 0, 0]
+
+
+def test_tiny_scale_groups(dev):
+    """FP8 groups whose amax lies far below the fp32 normal range: codes and scales must be
+    bit-exact with the oracle (the quotient, 1/scale and the rounding remainder must not
+    overflow or underflow), in the fused call and in the quant alone."""
+    rng = np.random.default_rng(71)
+    d = make_inputs(CONFIGS["tiny"], seed=71, R=2, T=8, H=1024)
+    d["gamma"] = _with_group_exponents(d["gamma"][None, :], TINY_GROUP_EXPONENTS, rng)[0]
+    u = Uploaded(d, dev)
+    for variant in ("latency", "bandwidth"):
+        _, _, rep = run_and_compare(u, True, variant, label="tiny-scale groups")
+        assert rep["n_code_diff"] == 0 and rep["max_scale_rel_err"] == 0.0, rep
+    x = _with_group_exponents(make_inputs(CONFIGS["tiny"], seed=72, R=1, T=16, H=1024)["residual"],
+                              TINY_GROUP_EXPONENTS, rng)
+    say("[gpu] quant alone, tiny-scale groups T=16 H=1024")
+    q, sc = F.quant_group(to_dev_bf16(x, dev))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_group(x)
+    rep = compare_fp8(q.cpu().numpy(), rq, sc.cpu().numpy(), rs)
+    assert rep["n_code_diff"] == 0 and rep["max_scale_rel_err"] == 0.0, rep
+
+
 def test_nan_row(dev):
     d = make_inputs(CONFIGS["tiny"], seed=60, R=2, T=4, H=256)
     d["partials"][1, 2, 5] = 0x7FC0

@@ -43,6 +43,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -139,37 +140,35 @@ __device__ __forceinline__ uint32_t pack_bf16_d(double lo, double hi) {
     return pack_bf16(f64_to_f32_odd(lo), f64_to_f32_odd(hi));
 }
 
-// OCP E4M3 code of the exact quotient o / scale (scale > 0 finite, inv ~ 1/scale),
-// rounded once to nearest even, saturating to +-448. Written from the format
-// definition: codes step by 2^(e-3) in [2^e, 2^(e+1)) for e >= -6 (3 mantissa bits;
-// exponent bias 7) and by 2^-9 below 2^-6.
-// v = o * inv is within a few fp32 units of the exact quotient: enough to find the
+// OCP E4M3 magnitude code (0..0x7E; 0x7F for NaN) of the exact quotient |o| / scale
+// (scale > 0, inv ~ 1/scale, both normal numbers), rounded once to nearest even and
+// saturated at 448. Written from the format definition: codes step by 2^(e-3) in
+// [2^e, 2^(e+1)) for e >= -6 (3 mantissa bits, exponent bias 7) and by 2^-9 below 2^-6.
+// v = |o| * inv is within a few fp32 units of the exact quotient: enough to find the
 // two codes around it (the truncated code `lo` and lo + 1) and the midpoint `mid`
-// between them, which is exact in fp32. Whether the exact quotient passes the
-// midpoint is decided exactly: o/scale >= mid  <=>  |o| - mid*scale >= 0, and one FMA
-// gives that difference with its sign intact. A tie (difference 0) goes to the even
-// code. If v sits a unit or two off, on the far side of a code value, the midpoint
-// test still lands on that code.
+// between them, which is exact in fp32. Whether the exact quotient passes the midpoint
+// is decided exactly: |o|/scale >= mid  <=>  d = |o| - mid*scale >= 0, and one FMA gives
+// d with its sign intact (+0 when it is exactly 0). The code is lo + 1 - neg with
+// neg = 1 when d < 0, or d = +0 (a tie) and lo is even: the integer sum bits(d) + odd - 1
+// is negative in exactly those cases. If v sits a unit or two off, on the far side of
+// a code value, the midpoint test still lands on that code.
 // Below 2^-6 the value is shifted up by 2^-6 first: in [2^-6, 2^-5) the top 3 mantissa
 // bits count steps of 2^-9, so the same bit slicing serves the subnormal grid, and the
-// shift comes back off exactly. Branch-free; no division per element.
-__device__ __forceinline__ uint32_t e4m3_code(float o, float scale, float inv) {
-    const float v = o * inv;
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t s = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    const bool sub = a < 0x3c800000u;                        // |v| < 2^-6
-    const float off = sub ? 0.015625f : 0.0f;                // 2^-6
-    const uint32_t xb = __float_as_uint(__uint_as_float(a) + off);
+// shift comes back off exactly. Any v at or above 448 (inf included) lands at or above
+// code 0x7E before the final clamp. Branch-free; no division per element.
+__device__ __forceinline__ uint32_t e4m3_mag(float o, float scale, float inv) {
+    const float ao = __builtin_fabsf(o);
+    const float a = ao * inv;
+    const bool sub = a < 0.015625f;                          // v < 2^-6
+    const float off = sub ? 0.015625f : 0.0f;
+    const uint32_t xb = __float_as_uint(a + off);
     const float mid = __uint_as_float((xb & 0xfff00000u) | 0x00080000u) - off;
-    const uint32_t lo = (xb >> 20) - (sub ? 968u : 960u);    // rebias 127 -> 7 (and -8 below 2^-6)
-    const float d = __builtin_fmaf(-mid, scale, __builtin_fabsf(o));
-    const uint32_t up = (d > 0.0f || (d == 0.0f && (lo & 1u) != 0u)) ? 1u : 0u;
-    uint32_t c = lo + up;                                    // 8 subnormal steps reach 0x08 = 2^-6
-    c = c > 0x7eu ? 0x7eu : c;
-    c = a >= 0x43e00000u ? 0x7eu : c;                        // |v| >= 448, inf: largest finite
-    c = a > 0x7f800000u ? 0x7fu : c;                         // NaN
-    return s | c;
+    const float d = __builtin_fmaf(-mid, scale, ao);
+    const uint32_t odd = (xb >> 20) & 1u;                    // parity of lo
+    const uint32_t neg = (__float_as_uint(d) + odd - 1u) >> 31;
+    // lo + 1 - neg, with lo = bits/2^20 less the rebias 127 -> 7 (and 8 steps below 2^-6)
+    const uint32_t c = min((xb >> 20) - (sub ? 967u : 959u) - neg, 0x7eu);
+    return __builtin_isnan(a) ? 0x7fu : c;
 }
 
 // FP4 E2M1 code (OCP Microscaling Formats (MX) v1.0: 1 sign, 2 exponent bits with
@@ -321,25 +320,38 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     return 1.0 / __builtin_sqrt(tot / (double)k.h + (double)k.eps);
 }
 
-// E4M3 codes of one vector slot (8 bf16 values as floats) and, from one lane per
-// 16-lane group, the group's scale, stored at byte sbase + group * sstride of r_sc.
-__device__ __forceinline__ void quant_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off,
-                                           uint32_t sbase, uint32_t sstride) {
-    uint32_t amax = 0u;
+// E4M3 codes of one vector slot (8 bf16 values, two per word of `ob`) and, from one lane
+// per 16-lane group, the group's scale, stored at byte sbase + group * sstride of r_sc.
+// The group's amax is a packed 16-bit max of the magnitude patterns (bf16 magnitudes
+// order as unsigned integers, inf included, and a NaN, above inf, wins and propagates
+// into the scale). Codes are computed on magnitudes; the element signs (the top bit of
+// bytes 1 and 3 of each pair word) are merged four at a time with one byte permute.
+// An all-zero group has scale 0 and every code +0: inv = 0 keeps its lanes on the
+// arithmetic path, and the sign mask is cleared. A group whose scale is below 2^-64 is
+// quantised from |o| and scale both times 2^64 (exact), so that 1/scale, the quotient
+// and the FMA remainder stay normal numbers; the stored scale is the unscaled one.
+__device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
+                                           uint32_t sstride) {
+    u16x2 m = u16x2{0, 0};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
-    amax = row16_umax(amax);  // 16 lanes = one 128-channel group
+    for (int w = 0; w < 4; ++w) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[w] & 0x7fff7fffu));
+    const uint32_t amax = row16_umax(max((uint32_t)m[0], (uint32_t)m[1])) << 16;  // 16 lanes = 128 channels
     const float scale = __uint_as_float(amax) / 448.0f;  // correctly rounded
-    // An all-zero group has scale 0 and all codes 0: inv = 0 keeps every lane on the
-    // arithmetic path (no per-element branch) and the mask clears the codes.
-    const float inv = scale == 0.0f ? 0.0f : 1.0f / scale;
-    const uint32_t keep = scale == 0.0f ? 0u : 0xffu;
+    const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
+    const float sk = scale * k;
+    const float inv = scale == 0.0f ? 0.0f : 1.0f / sk;
     uint32_t c[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = e4m3_code(o[e], scale, inv) & keep;
+    for (int w = 0; w < 4; ++w) {
+        c[2 * w] = e4m3_mag(bf_lo(ob[w]) * k, sk, inv);
+        c[2 * w + 1] = e4m3_mag(bf_hi(ob[w]) * k, sk, inv);
+    }
+    const uint32_t smask = scale == 0.0f ? 0u : 0x80808080u;
     u32x2 codes;
-    codes[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    codes[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    codes[0] = (c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24)) |
+               (__builtin_amdgcn_perm(ob[1], ob[0], 0x07050301u) & smask);
+    codes[1] = (c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)) |
+               (__builtin_amdgcn_perm(ob[3], ob[2], 0x07050301u) & smask);
     st8(codes, r_q, off >> 1);
     // one lane per group writes the scale; the others aim past the row (dropped)
     const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off >> 8) * sstride : kDropOffset;
@@ -386,7 +398,7 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
         o[2 * w + 1] = bf_hi(packed[w]);
     }
     st16(packed, r_out, off);
-    if constexpr (QM == kQuantFp8) quant_slot(o, r_q, r_sc, off, sbase, sstride);
+    if constexpr (QM == kQuantFp8) quant_slot(packed, r_q, r_sc, off, sbase, sstride);
     if constexpr (QM == kQuantMxfp4) mxfp4_slot(o, r_q, r_sc, off);
 }
 
@@ -483,15 +495,7 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) xv[v] = ld16(r_x, (v * blockDim.x + threadIdx.x) * 16u);
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        float o[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            o[2 * w] = bf_lo(xv[v][w]);
-            o[2 * w + 1] = bf_hi(xv[v][w]);
-        }
-        quant_slot(o, r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
-    }
+    for (int v = 0; v < VPL; ++v) quant_slot(xv[v], r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
 }
 
 // ---------------------------------------------------------------- dispatch tables
@@ -536,20 +540,7 @@ KernelFn pick(int R, int vi) {
 
 namespace farn {
 
-int launch(const Call &c, int variant) {
-    const RowShape rs = row_shape(c.H, c.kind == Kind::kFused ? variant : 1);
-    const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
-    KernelFn fn = nullptr;
-    if (c.kind == Kind::kReduce) {
-        fn = pick_reduce(c.R, vi);
-    } else if (c.kind == Kind::kQuant) {
-        fn = kQuantRows[vi];
-    } else {
-        fn = c.q == nullptr ? pick<kQuantNone>(c.R, vi)
-                            : (c.mxfp4 ? pick<kQuantMxfp4>(c.R, vi) : pick<kQuantFp8>(c.R, vi));
-    }
-    if (!fn) return 1;
-
+static Params make_params(const Call &c) {
     Params k;
     for (int r = 0; r < 8; ++r) k.p[r] = c.partials[r];
     k.res = c.residual;
@@ -565,6 +556,24 @@ int launch(const Call &c, int variant) {
     k.ngroups = (int)(c.H / 128);
     k.h = (double)c.H;
     k.eps = c.eps;
+    return k;
+}
+
+int launch(const Call &c, int variant) {
+    const RowShape rs = row_shape(c.H, c.kind == Kind::kFused ? variant : 1);
+    const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
+    KernelFn fn = nullptr;
+    if (c.kind == Kind::kReduce) {
+        fn = pick_reduce(c.R, vi);
+    } else if (c.kind == Kind::kQuant) {
+        fn = kQuantRows[vi];
+    } else {
+        fn = c.q == nullptr ? pick<kQuantNone>(c.R, vi)
+                            : (c.mxfp4 ? pick<kQuantMxfp4>(c.R, vi) : pick<kQuantFp8>(c.R, vi));
+    }
+    if (!fn) return 1;
+
+    const Params k = make_params(c);
     hipLaunchKernelGGL(fn, dim3((uint32_t)c.T), dim3((uint32_t)rs.lanes), 0, (hipStream_t)c.stream, k);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
