@@ -57,10 +57,16 @@ def test_status_strings_and_select():
     for T in (1, 2, 64, 512, 4096, 8192, 1 << 20):
         for H in (256, 7168, 8192):
             assert F.select_variant(8, T, H, False) in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH)
-    assert F.select_variant(8, 64, 7168, False) == F.VARIANT_LATENCY  # decode
-    assert F.select_variant(8, 16, 4096, True) == F.VARIANT_LATENCY  # decode FP8
-    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_BANDWIDTH  # prefill (measured best)
-    assert F.select_variant(8, 8192, 8192, False) == F.VARIANT_LATENCY  # wide wins at H = 8192
+    # the measured rule
+    assert F.select_variant(8, 64, 7168, False) == F.VARIANT_BANDWIDTH  # decode, H = 7168
+    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_BANDWIDTH  # FP8 prefill chunk
+    assert F.select_variant(8, 1, 8192, True) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(4, 16, 4096, True) == F.VARIANT_LATENCY  # decode FP8, H = 4096
+    assert F.select_variant(8, 8192, 4096, False) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 512, 6144, True) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 4096, 2048, False) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 8192, 2048, False) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(8, 8192, 1024, False) == F.VARIANT_LATENCY  # one wave per row
 
 
 class FakeCall:
