@@ -174,18 +174,20 @@ __device__ __forceinline__ uint32_t e4m3_mag(float o, float scale, float inv) {
 // FP4 E2M1 code (OCP Microscaling Formats (MX) v1.0: 1 sign, 2 exponent bits with
 // bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) of x, which is exact
 // (a bf16 value times a power of two), rounded once to nearest even, magnitudes above 6
-// clamped to 6. The grid step is 0.5 below 2, 1 in [2, 4) and 2 in [4, 8); on each
-// piece the code is an offset plus rint(x / step), and ties to an even multiple of the
-// step are ties to the even code.
+// clamped to 6. From 1 up the codes are the fp32 numbers with 2 significant bits, so
+// rounding |x|'s bit pattern to 2 significant bits (add half a unit less one, plus the
+// last kept bit, then drop 22 bits) rounds to nearest with ties to the even code, and
+// the kept bits less the rebias 127 -> 1 are the code (6 < |x| < 7 rounds to 6, 7 and up
+// to 8 or beyond, which the clamp takes back to 6). Below 1 the grid step is 0.5 - the
+// step of 2-bit numbers in [1, 2) - so |x| + 1 rounds the same way and the code is the
+// kept bits less the pattern of 1. Branch-free.
 __device__ __forceinline__ uint32_t e2m1_code(float x) {
-    const uint32_t s = (__float_as_uint(x) >> 28) & 0x8u;
     const float a = __builtin_fabsf(x);
-    const float c0 = __builtin_rintf(a * 2.0f);          // codes 0..4 for a < 2
-    const float c1 = __builtin_rintf(a) + 2.0f;          // codes 4..6 for 2 <= a < 4
-    const float c2 = __builtin_rintf(a * 0.5f) + 4.0f;   // codes 6..8 for 4 <= a < 8
-    float c = a < 2.0f ? c0 : (a < 4.0f ? c1 : c2);
-    c = a >= 6.0f ? 7.0f : c;
-    return s | (uint32_t)c;
+    const bool small = a < 1.0f;
+    const uint32_t b = __float_as_uint(a + (small ? 1.0f : 0.0f));
+    const uint32_t kept = (b + 0x1fffffu + ((b >> 22) & 1u)) >> 22;
+    const uint32_t c = min(kept - (small ? 254u : 252u), 7u);
+    return ((__float_as_uint(x) >> 28) & 0x8u) | c;
 }
 
 // ---------------------------------------------------------------- cross-lane
