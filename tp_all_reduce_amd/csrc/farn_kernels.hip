@@ -157,6 +157,9 @@ __device__ __forceinline__ uint32_t pack_bf16_d(double lo, double hi) {
 // shift comes back off exactly. Any v at or above 448 (inf included) lands at or above
 // code 0x7E before the final clamp. Branch-free; no division per element.
 __device__ __forceinline__ uint32_t e4m3_mag(float o, float scale, float inv) {
+    // each step rounds on its own, as written (no mul + add contraction into an FMA): the
+    // exhaustive CPU check of this encoder models exactly this sequence
+#pragma clang fp contract(off)
     const float ao = __builtin_fabsf(o);
     const float a = ao * inv;
     const bool sub = a < 0.015625f;                          // v < 2^-6
@@ -182,6 +185,7 @@ __device__ __forceinline__ uint32_t e4m3_mag(float o, float scale, float inv) {
 // step of 2-bit numbers in [1, 2) - so |x| + 1 rounds the same way and the code is the
 // kept bits less the pattern of 1. Branch-free.
 __device__ __forceinline__ uint32_t e2m1_code(float x) {
+#pragma clang fp contract(off)
     const float a = __builtin_fabsf(x);
     const bool small = a < 1.0f;
     const uint32_t b = __float_as_uint(a + (small ? 1.0f : 0.0f));
