@@ -127,11 +127,12 @@ farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, co
                                           void *stream);
 
 /* Launch shapes of the one kernel (one workgroup per token row). AUTO picks by size
-   (farn_select_variant). LATENCY: the widest row mapping (up to 1024 lanes, one 16-byte
-   vector per lane up to H = 8192), the shortest per-row chain, for small T. BANDWIDTH:
-   about half as many lanes with two vectors each (4096 < H <= 8192), so several rows
-   share a CU, for large T. Both compute the same results (their fp64 sums of squares
-   differ only in the order of additions). */
+   from measurements (farn_select_variant). LATENCY: the widest row mapping (up to 1024
+   lanes, one 16-byte vector per lane up to H = 8192). BANDWIDTH: about half as many lanes
+   with two vectors each (for 1024 < H <= 8192; the same as LATENCY otherwise). Which is
+   faster depends on how evenly the row's waves fill a compute unit's four SIMDs, not on T
+   alone: AUTO takes BANDWIDTH for H = 7168 and 8192 at every T. Both compute the same
+   results (their fp64 sums of squares differ only in the order of additions). */
 typedef enum farn_variant {
     FARN_VARIANT_AUTO = 0,
     FARN_VARIANT_LATENCY = 1,
