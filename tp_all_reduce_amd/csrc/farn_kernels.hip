@@ -13,22 +13,21 @@
 //   lane-strided: lane l holds vectors l, l+L, l+2L, ... So every load instruction of a
 //   wave is 64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is
 //   exactly 16 consecutive lanes (one DPP row) of one vector slot.
-//   Per lane: the loads of the row's slots are issued before any is consumed; the
-//   partials are summed in fp32 in rank order, the residual added last, the sum
+//   Per lane: the source issues the loads of the row's slots before consuming any (the
+//   compiler may still sink some below the first slot's fold); the partials are summed in fp32 in rank order, the residual added last, the sum
 //   rounded to bf16 (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
 //   per wave through LDS -> every wave adds the per-wave values in wave order; the
 //   normalisation product is fp64 too, rounded once to bf16. The row never passes
 //   through LDS; only one double per wave does.
 //
-// Two launch shapes of the same kernel (chosen by the host from T and H):
+// Two launch shapes of the same kernel (chosen by the host from T and H, as measured):
 //   latency   - the widest row mapping (L up to 1024, one vector per lane up to H =
-//               8192): the fewest dependent instructions per lane, for small T where
-//               a row's own latency is the call's latency (decode).
-//   bandwidth - a narrow mapping (L about NV/2, two vectors per lane, both issued up
-//               front): workgroups of about 7 waves, so several rows share a CU and one
-//               row's arithmetic overlaps another's loads (prefill). On MI355X this
-//               moves the FP8 prefill call from 225 to 214 us.
+//               8192): the fewest instructions per lane.
+//   bandwidth - a narrow mapping (L about NV/2, two vectors per lane): half the waves
+//               per row, which fill a compute unit's four SIMDs differently. On MI355X it
+//               is the faster one for H = 7168 and 8192 at every T (the FP8 prefill call
+//               at H = 7168: 212 against 223 us), the slower one for H = 3072 .. 6144.
 // The fp64 statistics make the two shapes agree bit for bit in practice (their sums
 // of squares differ only in the order of fp64 additions).
 //
@@ -409,9 +408,9 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
 }
 
 // Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
-// lane the second slot's loads are issued before the first is reduced; with four (rows
-// beyond 16384 channels) the slots are loaded and reduced one after the other, to bound
-// register use.
+// lane the source issues the second slot's loads before reducing the first; with four
+// (rows beyond 16384 channels) the slots are loaded and reduced one after the other, to
+// bound register use.
 template <int R, int VPL, int QM>
 __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
                                        const Params &k, int64_t t, double *slot) {
