@@ -15,8 +15,8 @@
  *                 double, sum in double
  *   5. normalise  out = bf16_rne(y * rstd * gamma), product in double, one rounding
  *   6. quant      per row and 128-channel group: amax = max |out|,
- *                 scale = fl32(amax / 448), q = e4m3fn_rne_satfinite(out / scale)
- *                 (division in double, one rounding); scale == 0 gives q = 0.
+ *                 scale = fl32(amax / 448), v = fl32(out / scale) (IEEE single
+ *                 division), q = e4m3fn_rne_satfinite(v); scale == 0 gives q = 0.
  *
  * Where the pages support these steps:
  *   - all-reduce then RMSNorm of the all-reduce output, returning both
@@ -39,6 +39,8 @@
  *   - one rounding of y*rstd*gamma;
  *   - quant input is the bf16 `out`; no floor on the scale; all-zero group gives
  *     scale 0 and codes 0;
+ *   - out / scale is a binary32 division (the division an fp32 framework performs
+ *     before casting to e4m3fn), and that quotient is rounded once more, to e4m3fn;
  *   - e4m3fn saturates to +-448 (it never has to for finite input, since
  *     |out/scale| <= 448 up to one fp32 rounding);
  *   - a NULL residual means "no residual" (zeros, the zero not added);
@@ -192,7 +194,7 @@ static void one_row(const job_t *j, int64_t t, uint16_t *o) {
                 if (scale == 0.0f)
                     j->q[base + h] = 0x00u;
                 else
-                    j->q[base + h] = oracle_e4m3fn_from_double(bf16_to_double(o[h]) / (double)scale);
+                    j->q[base + h] = oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale));
             }
         }
     }
@@ -304,7 +306,7 @@ int oracle_quant_group(const uint16_t *x, int64_t T, int64_t H, int group, uint8
             scales[t * G + g] = scale;
             for (int64_t h = 0; h < group; ++h)
                 q[t * H + g * group + h] =
-                    scale == 0.0f ? 0x00u : oracle_e4m3fn_from_double(bf16_to_double(o[h]) / (double)scale);
+                    scale == 0.0f ? 0x00u : oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale));
         }
     }
     return 0;

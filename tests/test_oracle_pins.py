@@ -312,16 +312,54 @@ def check_quant_scale_and_max_code():
         assert np.all((qq == 0x7E).any(axis=2) | (amax == 0))
 
 
+def _fp32_quotient(bits, s) -> Fraction:
+    """out/scale as a binary32 division (numpy's IEEE single division), as an exact rational."""
+    return Fraction(float(np.float32(bf16_bits_to_float(np.uint16(bits))) / np.float32(s)))
+
+
 def check_quant_codes_exact_small():
-    """Codes equal the nearest E4M3 (by search) to the exact quotient out/scale, on tiny shapes."""
+    """Codes equal the nearest E4M3 (by search over the decoded code table) to the binary32
+    quotient out/scale, on tiny shapes."""
     for seed, R, T, H in [(3, 2, 2, 128), (4, 4, 1, 256)]:
         d, (ro, out, q, sc) = _quant_case(seed, R, T, H)
         for t in range(T):
             for h in range(H):
-                s = sc[t, h // 128]
-                v = bf16_bits_to_fraction(out[t, h]) / Fraction(float(s))
+                v = _fp32_quotient(out[t, h], sc[t, h // 128])
                 want = e4m3fn_nearest(v, negative_zero=(out[t, h] == 0x8000))
                 assert q[t, h] == want, (t, h, q[t, h], want)
+
+
+def check_quant_fp32_quotient_ties():
+    """Where the binary32 quotient out/scale is exactly an E4M3 tie but the rational quotient is
+    not, the two readings of out/scale round to different codes: the codes must follow the
+    binary32 quotient. Every bf16 value of a few groups (scales not powers of two) is scanned for
+    such points with the midpoints of the decoded code table."""
+    codes = [c for c in range(0x7F) if e4m3fn_decode(c) is not None]
+    vals = sorted(e4m3fn_decode(c) for c in codes)
+    mids = np.array([float((a + b) / 2) for a, b in zip(vals, vals[1:])])
+    found = 0
+    for amax_f in (1.0, 3.0, 0.6875, 1.9375e-3, 37.5):
+        amax_b = int(f2b(np.array([amax_f]))[0])
+        s = np.float32(bf16_bits_to_float(np.uint16(amax_b))) / np.float32(448.0)
+        obits = np.arange(1, amax_b + 1, dtype=np.uint16)                 # every bf16 value in (0, amax]
+        of = bf16_bits_to_float(obits).astype(np.float32)
+        v32 = (of / s).astype(np.float32)
+        hit = np.nonzero(np.isin(v32.astype(np.float64), mids) &
+                         (v32.astype(np.float64) != of.astype(np.float64) / np.float64(s)))[0]
+        if hit.size == 0:
+            continue
+        x = np.zeros((len(hit), 128), np.uint16)
+        x[:, 0] = amax_b
+        x[:, 1] = obits[hit]
+        q, sc = oracle.quant_group(x)
+        assert np.all(sc[:, 0] == s)
+        for i, j in enumerate(hit):
+            vq = _fp32_quotient(obits[j], s)
+            vr = Fraction(float(of[j])) / Fraction(float(s))
+            want = e4m3fn_nearest(vq)
+            assert q[i, 1] == want, (amax_f, float(of[j]), q[i, 1], want)
+            found += int(want != e4m3fn_nearest(vr))
+    assert found >= 5, found
 
 
 def check_quant_dequant_bound():
@@ -385,7 +423,7 @@ def check_reduce_alone():
 
 def check_quant_alone():
     """Quant alone on bf16 inputs with outliers: scale = IEEE single amax/448, a 448 code in every
-    nonzero group, codes = exact nearest E4M3 of the rational quotient, zero groups give zeros."""
+    nonzero group, codes = nearest E4M3 of the binary32 quotient, zero groups give zeros."""
     rng = np.random.default_rng(8)
     x = rng.standard_normal((4, 512)).astype(np.float32)
     x[:, rng.choice(512, 6, replace=False)] *= 20
@@ -402,7 +440,7 @@ def check_quant_alone():
             s = sc[t, h // 128]
             if s == 0:
                 continue
-            v = bf16_bits_to_fraction(xb[t, h]) / Fraction(float(s))
+            v = _fp32_quotient(xb[t, h], s)
             assert q[t, h] == e4m3fn_nearest(v, negative_zero=(xb[t, h] == 0x8000)), (t, h)
 
 
@@ -504,7 +542,8 @@ ALL_CHECKS = [
     check_integer_sums_exact, check_fold_order_and_precision, check_identities, check_reduce_vs_exact_sum,
     check_norm_vs_exact, check_constant_rows, check_vs_torch_rms_norm, check_constant_gamma_rms,
     check_scale_invariance,
-    check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_dequant_bound,
+    check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_fp32_quotient_ties,
+    check_quant_dequant_bound,
     check_quant_zero_group_and_consistency, check_in_place_residual,
     check_reduce_alone, check_quant_alone,
     check_e2m1_encoder, check_mxfp4_blocks, check_mxfp4_fused_consistency,
@@ -557,6 +596,10 @@ MUTANTS = [
     ("quant_alone_scale_240", "float scale = (float)(amax / 448.0);\n            scales[t * G + g] = scale;",
      "float scale = (float)(amax / 240.0);\n            scales[t * G + g] = scale;"),
     ("quant_alone_wrong_group_base", "const uint16_t *o = x + t * H + g * group;", "const uint16_t *o = x + t * H;"),
+    ("quotient_in_double", "oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale))",
+     "oracle_e4m3fn_from_double(bf16_to_double(o[h]) / (double)scale)",
+     "oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale))",
+     "oracle_e4m3fn_from_double(bf16_to_double(o[h]) / (double)scale)"),
     ("mx_emax_3", "int s = (e2 - 1) - 2;", "int s = (e2 - 1) - 3;"),
     ("mx_nibbles_swapped", "(uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4))", "(uint8_t)(codes[2 * i + 1] | (codes[2 * i] << 4))"),
     ("mx_no_saturation", "if (a >= 6.0) return (uint8_t)(sign | 0x7u);", "if (a >= 1e30) return (uint8_t)(sign | 0x7u);",
