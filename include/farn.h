@@ -26,8 +26,9 @@
  *   out[t,h] = bf16_rne((residual_out[t,h] * rstd) * gamma[h])   fp64 product, one rounding
  * and for the quant call, per group g of 128 channels:
  *   scale[t,g] = amax_g |out| / 448  (fp32, correctly rounded)
- *   q[t,h]     = e4m3fn_rne(out[t,h] / scale[t,g])  (OCP E4M3, satfinite; 0 when scale == 0;
- *                one rounding of the exact quotient)
+ *   q[t,h]     = e4m3fn_rne(fl32(out[t,h] / scale[t,g]))  (OCP E4M3, satfinite; 0 when
+ *                scale == 0; the quotient as an IEEE single division gives it, then one
+ *                rounding to E4M3)
  *
  * Layout: every [T,H] buffer is row-major and contiguous (row stride H
  * elements); bf16 values are passed as raw 16-bit patterns; q holds one E4M3
@@ -180,8 +181,8 @@ farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H
                         void *stream);
 
 /* Per-group quant alone of a bf16 [T,H] input x: scales[t,g] = amax/448 over channels
- * [128g, 128g+128) of row t, q = E4M3 codes of x/scale (one rounding, satfinite, 0 for a
- * zero group). group_size must be 128; H % 128 == 0; q and scales may not overlap x. */
+ * [128g, 128g+128) of row t, q = E4M3 codes of fl32(x/scale) (as in the FP8 call;
+ * satfinite, 0 for a zero group). group_size must be 128; H % 128 == 0; q and scales may not overlap x. */
 farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
                              float *scales, void *stream);
 

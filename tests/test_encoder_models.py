@@ -8,14 +8,13 @@ with the oracle's encoder of the exact value. A model is only as faithful as its
 a change to either device function must be repeated here.
 
 fp32 steps map one to one onto numpy float32 operations (round to nearest even, subnormals
-kept). The one FMA is modelled by its sign and zero-ness, which is all the encoder reads:
-mid*scale is exact in binary64 (24 + 24 bits), so the binary64 difference |o| - mid*scale has
-the exact difference's sign and is zero only when it is; the fp32 result is that difference
-rounded once (modelled by rounding the binary64 value; the two can differ only for a nonzero
-difference within a factor 2 of 2^-150, far below any group scale tested here).
+kept); fp32 FMAs are modelled exactly (`_fma32`). The E4M3 reference is the oracle's encoder of
+the binary32 quotient out/scale (numpy's IEEE single division).
 """
 
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -24,32 +23,49 @@ import oracle
 F32 = np.float32
 
 
-def e4m3_mag_model(o: np.ndarray, scale: np.float32, inv: np.float32) -> np.ndarray:
-    """Model of `e4m3_mag(o, scale, inv)`: magnitude code of |o| / scale."""
+def _fma32(a, b, c) -> np.ndarray:
+    """fp32 FMA a*b + c with one rounding, for arrays of one shape. a*b is exact in binary64
+    (24 + 24 bits); the binary64 sum is re-done in exact rationals wherever its result sits on
+    an fp32 rounding boundary (the only place rounding it again could differ from one rounding)."""
+    a64, b64, c64 = (np.asarray(x, np.float32).astype(np.float64) for x in (a, b, c))
+    x = a64 * b64 + c64
+    with np.errstate(over="ignore", invalid="ignore"):
+        out = x.astype(np.float32)
+    edge = np.isfinite(x) & ((x.view(np.uint64) & np.uint64((1 << 29) - 1)) == np.uint64(1 << 28))
+    for i in np.nonzero(edge)[0]:
+        exact = Fraction(float(a64[i])) * Fraction(float(b64[i])) + Fraction(float(c64[i]))
+        y = out[i]
+        cands = [np.nextafter(y, F32(-np.inf)), y, np.nextafter(y, F32(np.inf))]
+        out[i] = min(cands, key=lambda v: (abs(Fraction(float(v)) - exact), int(np.array(v).view(np.uint32)) & 1))
+    return out
+
+
+def e4m3_mag_model(o: np.ndarray, scale_r: np.float32, inv: np.float32) -> np.ndarray:
+    """Model of `e4m3_mag(o, scale_r, inv)`: magnitude code of fl32(|o| / scale)."""
     ao = np.abs(o.astype(np.float32))
     with np.errstate(invalid="ignore", over="ignore"):
-        a = (ao * F32(inv)).astype(np.float32)
-        sub = a < F32(2.0 ** -6)
-        off = np.where(sub, F32(2.0 ** -6), F32(0.0)).astype(np.float32)
-        xb = (a + off).astype(np.float32).view(np.uint32)
-        mid = (((xb & np.uint32(0xFFF00000)) | np.uint32(0x00080000)).view(np.float32) - off).astype(np.float32)
-        d = (-mid.astype(np.float64) * np.float64(scale) + ao.astype(np.float64)).astype(np.float32)
-    odd = ((xb >> np.uint32(20)) & np.uint32(1)).astype(np.uint64)
-    neg = ((d.view(np.uint32).astype(np.uint64) + odd + 0xFFFFFFFF) & 0xFFFFFFFF) >> 31
-    c = (xb >> np.uint32(20)).astype(np.int64) - np.where(sub, 967, 959) - neg.astype(np.int64)
-    c = np.minimum(c, 0x7E)
-    return np.where(np.isnan(a), 0x7F, c).astype(np.uint8)
+        q0 = (ao * F32(inv)).astype(np.float32)
+        r = _fma32(-q0, np.full_like(q0, scale_r), ao)
+        v = _fma32(r, np.full_like(q0, inv), q0)
+        b = v.view(np.uint32).astype(np.uint64)
+        cn = (((b + 0x7FFFF + ((b >> 20) & 1)) >> 20) & 0xFFFFFFFF).astype(np.int64) - 960
+        cs = np.rint((v * F32(512.0)).astype(np.float32))
+        cs = np.where(np.isfinite(cs), cs, 0).astype(np.int64)
+    c = np.minimum(np.where(v < F32(2.0 ** -6), cs, cn), 0x7E)
+    return np.where(np.isnan(v), 0x7F, c).astype(np.uint8)
 
 
 def group_codes_model(o: np.ndarray, amax: np.float32) -> tuple[np.ndarray, np.float32]:
     """Model of `quant_slot`'s per-group arithmetic for a group with max magnitude amax:
-    scale = amax/448 correctly rounded, the 2^64 rescaling of tiny groups, inv = 1/scale."""
+    scale = amax/448 correctly rounded, the 2^64 rescaling of tiny groups, inv = 1/scale, the
+    remainder's scale clamped to the largest finite float."""
     scale = F32(np.float64(amax) / 448.0)  # amax/448 is never a tie in fp32, so one rounding
     k = F32(2.0 ** 64) if scale < F32(2.0 ** -64) else F32(1.0)
     sk = F32(scale * k)
     with np.errstate(divide="ignore"):
         inv = F32(0.0) if scale == 0 else F32(1.0) / sk
-    return e4m3_mag_model((o.astype(np.float32) * k).astype(np.float32), sk, inv), scale
+    sr = min(sk, np.finfo(np.float32).max)
+    return e4m3_mag_model((o.astype(np.float32) * k).astype(np.float32), F32(sr), inv), scale
 
 
 def e2m1_model(x: np.ndarray) -> np.ndarray:
@@ -83,7 +99,9 @@ def _check_e4m3_groups(amax_patterns: np.ndarray) -> int:
         amax = np.array([ab << 16], np.uint32).view(np.float32)[0]
         o = FINITE_BF16[np.abs(FINITE_BF16) <= amax]      # every bf16 value the group can hold
         got, scale = group_codes_model(o, amax)
-        ref = oracle.e4m3fn_from_double_array(o.astype(np.float64) / np.float64(scale)) & 0x7F
+        with np.errstate(divide="ignore"):
+            v32 = (o / scale).astype(np.float32)              # IEEE single division
+        ref = oracle.e4m3fn_from_double_array(v32.astype(np.float64)) & 0x7F
         bad = np.nonzero(got != ref)[0]
         assert bad.size == 0, (f"amax {amax!r}: o={o[bad[0]]!r} model {got[bad[0]]:#x} "
                                f"oracle {ref[bad[0]]:#x} ({bad.size} differ)")
@@ -93,14 +111,18 @@ def _check_e4m3_groups(amax_patterns: np.ndarray) -> int:
 
 def test_e4m3_encoder_model():
     """Every finite bf16 value each group can hold, for ~3,300 group maxima (every subnormal
-    one included): about 10^8 pairs, a few seconds."""
+    one included): about 10^8 pairs, some seconds."""
     assert _check_e4m3_groups(_amax_patterns(3000, seed=1)) > 100_000_000
 
 
 def test_e4m3_encoder_model_specials():
-    # NaN quotient -> 0x7F; inf and anything at or above 448 -> 0x7E; zero -> 0
-    got = e4m3_mag_model(np.array([np.nan, np.inf, 448.0, 464.0, 1e30, 0.0], np.float32), F32(1.0), F32(1.0))
-    assert got.tolist() == [0x7F, 0x7E, 0x7E, 0x7E, 0x7E, 0]
+    # NaN -> 0x7F; anything at or above 448 -> 0x7E; zero -> 0; the tie 2^-10 -> 0, 3*2^-10 -> 2
+    got = e4m3_mag_model(np.array([np.nan, 448.0, 464.0, 1e30, 0.0, 2.0 ** -10, 3 * 2.0 ** -10], np.float32),
+                         F32(1.0), F32(1.0))
+    assert got.tolist() == [0x7F, 0x7E, 0x7E, 0x7E, 0, 0, 2]
+    # an inf group (scale inf, inv 0): finite values give 0, an infinite one NaN -> 0x7F
+    codes, scale = group_codes_model(np.array([3.0, np.inf], np.float32), F32(np.inf))
+    assert np.isinf(scale) and codes.tolist() == [0, 0x7F]
     # an all-zero group: scale 0, inv 0, every magnitude code 0
     codes, scale = group_codes_model(np.array([0.0, -0.0], np.float32), F32(0.0))
     assert scale == 0 and codes.tolist() == [0, 0]
