@@ -63,6 +63,8 @@ def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
     u8p = ctypes.POINTER(ctypes.c_uint8)
     L.oracle_e2m1_from_double.argtypes = [ctypes.c_double]
     L.oracle_e2m1_from_double.restype = ctypes.c_uint8
+    L.oracle_e2m1_from_double_array.argtypes = [dp, ctypes.POINTER(ctypes.c_uint8), ctypes.c_int64]
+    L.oracle_e2m1_from_double_array.restype = None
     L.oracle_mxfp4.argtypes = [u16p, ctypes.c_int64, ctypes.c_int64, u8p, u8p]
     L.oracle_mxfp4.restype = ctypes.c_int
     L.oracle_reduce_add_rmsnorm_mxfp4.argtypes = [
@@ -205,6 +207,14 @@ def quant_group(x, group: int = 128):
 
 def e2m1_from_double(x: float) -> int:
     return int(lib().oracle_e2m1_from_double(float(x)))
+
+
+def e2m1_from_double_array(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty(x.shape, np.uint8)
+    lib().oracle_e2m1_from_double_array(x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                        y.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), x.size)
+    return y
 
 
 def mxfp4(x):

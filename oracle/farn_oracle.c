@@ -345,6 +345,10 @@ uint8_t oracle_e2m1_from_double(double x) {
     return (uint8_t)(sign | 0x7u); /* r == 8 (from [7, 8)): clamp to 6 */
 }
 
+void oracle_e2m1_from_double_array(const double *x, uint8_t *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = oracle_e2m1_from_double(x[i]);
+}
+
 /* MXFP4 of a bf16 [T,H] input: q [T, H/2] bytes (two codes each), scales [T, H/32] E8M0 bytes. */
 int oracle_mxfp4(const uint16_t *x, int64_t T, int64_t H, uint8_t *q, uint8_t *scales) {
     if (!x || !q || !scales || T < 0 || H < 32 || H % 32 != 0) return -1;

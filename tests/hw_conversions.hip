@@ -1,0 +1,45 @@
+/*
+ * Test kernels for the GPU conversion instructions the FP8 and MXFP4 paths rely on
+ * (tests/test_gpu_conversions.py): v_cvt_pk_fp8_f32 over a range of fp32 bit patterns,
+ * and v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent.
+ * Built by tp_all_reduce_amd/build.py; not part of the library.
+ */
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// out[i] = E4M3 code of the fp32 with bit pattern base + i, i < n (n even)
+__global__ void fp8_of_bits(uint32_t base, uint8_t *out, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (2 * i + 1 >= n) return;
+    const float a = __uint_as_float(base + 2 * i), b = __uint_as_float(base + 2 * i + 1);
+    const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    out[2 * i] = (uint8_t)(w & 0xffu);
+    out[2 * i + 1] = (uint8_t)((w >> 8) & 0xffu);
+}
+
+// out[(s + 127) * n + i] = E2M1 code of x[i] * 2^-s, for s = -127 .. 127 (blockIdx.y), n even;
+// the scale operand is the fp32 whose exponent field is the E8M0 byte s + 127
+__global__ void fp4_all_scales(const float *x, uint8_t *out, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (2 * i + 1 >= n) return;
+    const float sc = __uint_as_float(blockIdx.y << 23);
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[2 * i], x[2 * i + 1], sc, 0);
+    const size_t base = (size_t)blockIdx.y * n;
+    out[base + 2 * i] = (uint8_t)(w & 0xfu);
+    out[base + 2 * i + 1] = (uint8_t)((w >> 4) & 0xfu);
+}
+
+extern "C" int hwconv_fp8_of_bits(uint32_t base, void *out, uint32_t n, void *stream) {
+    if (n == 0 || (n & 1u) || n > (1u << 28) || (uint64_t)base + n > 0x100000000ull) return 1;
+    const uint32_t block = 256, grid = (n / 2 + block - 1) / block;
+    hipLaunchKernelGGL(fp8_of_bits, dim3(grid), dim3(block), 0, (hipStream_t)stream, base, (uint8_t *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int hwconv_fp4_all_scales(const void *x, void *out, uint32_t n, void *stream) {
+    if (n == 0 || (n & 1u) || n > (1u << 20)) return 1;
+    const uint32_t block = 256, grid = (n / 2 + block - 1) / block;
+    hipLaunchKernelGGL(fp4_all_scales, dim3(grid, 255), dim3(block), 0, (hipStream_t)stream, (const float *)x,
+                       (uint8_t *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}

@@ -1,0 +1,86 @@
+"""The GPU conversion instructions the quant paths rely on, checked exhaustively against the
+oracle's encoders (which follow the format definitions).
+
+- v_cvt_pk_fp8_f32 (the FP8 call's codes): every fp32 value in [0, 464) and in (-464, -2^-10]
+  converts to the round-to-nearest-even OCP E4M3 code. The FP8 path only ever converts
+  quotients of magnitude below 464.
+- v_cvt_scalef32_pk_fp4_f32 (the MXFP4 call's codes): every non-NaN bf16 value x under every
+  E8M0 block exponent s = -127 .. 127 converts to the E2M1 code of x * 2^-s, round to nearest
+  even code, saturating at 6.
+
+Test kernels: tests/hw_conversions.hip (built into tests/libhwconv.so by the package build).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhwconv.so")
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def hw():
+    if not os.path.exists(LIB_PATH):
+        pytest.fail("tests/libhwconv.so is not built (python tp_all_reduce_amd/build.py builds it)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.hwconv_fp8_of_bits.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    L.hwconv_fp4_all_scales.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    return L
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+@pytest.mark.parametrize("lo,hi", [(0x00000000, 0x43E80000), (0xBA800000, 0xC3E80000)],
+                         ids=["positive_below_464", "negative_to_-464"])
+def test_fp8_conversion_is_rne_e4m3(hw, lo, hi):
+    chunk = 1 << 26
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    for base in range(lo, hi, chunk):
+        n = min(chunk, hi - base) & ~1
+        say(f"[gpu] v_cvt_pk_fp8_f32 over fp32 patterns {base:#010x} .. {base + n:#010x}")
+        assert hw.hwconv_fp8_of_bits(base, out.data_ptr(), n, _stream()) == 0
+        torch.cuda.synchronize()
+        got = out[:n].cpu().numpy()
+        x = np.arange(base, base + n, dtype=np.uint64).astype(np.uint32).view(np.float32).astype(np.float64)
+        want = oracle.e4m3fn_from_double_array(x)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, (f"{bad.size} codes differ, first x={x[bad[0]]!r}: "
+                               f"conversion {got[bad[0]]:#04x}, RNE E4M3 {want[bad[0]]:#04x}")
+
+
+def test_fp4_scaled_conversion_is_rne_e2m1(hw):
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    x = np.ascontiguousarray(x[~np.isnan(x)])
+    if x.size % 2:
+        x = np.append(x, np.float32(0.0))
+    n = x.size
+    say(f"[gpu] v_cvt_scalef32_pk_fp4_f32: {n} bf16 values x 255 block exponents")
+    xd = torch.from_numpy(x).to("cuda")
+    out = torch.empty(n * 255, dtype=torch.uint8, device="cuda")
+    assert hw.hwconv_fp4_all_scales(xd.data_ptr(), out.data_ptr(), n, _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(255, n)
+    x64 = x.astype(np.float64)
+    for k in range(255):
+        s = k - 127
+        want = oracle.e2m1_from_double_array(np.ldexp(x64, -s))
+        bad = np.nonzero(got[k] != want)[0]
+        assert bad.size == 0, (f"s={s}: {bad.size} codes differ, first x={x64[bad[0]]!r}: "
+                               f"conversion {got[k][bad[0]]:#x}, E2M1 {want[bad[0]]:#x}")

@@ -7,7 +7,8 @@
 The C-ABI layer (csrc/farn_api.cpp) makes no HIP call and is compiled by g++; the
 kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two. The plain C
 client of the ABI that the GPU tests run (tests/c_abi_client.c) is compiled by gcc
-against include/farn.h and the built library.
+against include/farn.h and the built library, and the test kernels of the conversion
+instructions (tests/hw_conversions.hip) by hipcc.
 """
 
 from __future__ import annotations
@@ -23,6 +24,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfarn.so")
 C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi_client.c")
 C_CLIENT = os.path.join(ROOT, "tests", "c_abi_client")
+HWCONV_SRC = os.path.join(ROOT, "tests", "hw_conversions.hip")
+HWCONV = os.path.join(ROOT, "tests", "libhwconv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
@@ -57,6 +60,7 @@ def build(verbose: bool = False) -> str:
     out += _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o])
     os.replace(tmp, LIB)
     out += build_c_client()
+    out += build_hwconv()
     if verbose:
         for ln in out:
             print(ln)
@@ -72,6 +76,14 @@ def build_c_client() -> list:
                 f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../tp_all_reduce_amd",
                 f"-Wl,-rpath,{ROCM}/lib"])
     os.replace(tmp, C_CLIENT)
+    return out
+
+
+def build_hwconv() -> list:
+    """The test kernels of the conversion instructions the quant paths use."""
+    tmp = HWCONV + f".tmp{os.getpid()}"
+    out = _run([HIPCC, *HIP_FLAGS, "-shared", "-o", tmp, HWCONV_SRC])
+    os.replace(tmp, HWCONV)
     return out
 
 

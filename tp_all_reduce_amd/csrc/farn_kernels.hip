@@ -139,55 +139,28 @@ __device__ __forceinline__ uint32_t pack_bf16_d(double lo, double hi) {
     return pack_bf16(f64_to_f32_odd(lo), f64_to_f32_odd(hi));
 }
 
-// OCP E4M3 magnitude code (0..0x7E; 0x7F for NaN) of v = fl32(|o| / scale): the quotient
-// rounded to fp32 as an IEEE single division rounds it, then rounded once more, to nearest
-// even E4M3, saturating at 448. Written from the format definition: codes step by 2^(e-3)
-// in [2^e, 2^(e+1)) for e >= -6 (3 mantissa bits, exponent bias 7) and by 2^-9 below 2^-6.
-// The division without a divide: q0 = |o| * inv (inv = 1/scale), the remainder
-// |o| - q0*scale by one FMA, and one correction q0 + r*inv by another. This v can sit one
-// fp32 unit from the correctly rounded quotient, but never where that changes the E4M3 code:
-// over every bf16 amax and every bf16 |o| <= amax (with the rescaling of tiny groups done by
-// the caller) the codes agree, 5.3e8 pairs checked on the CPU.
-// Rounding v: from 2^-6 up, add half a unit of the 3-bit mantissa less one plus the last
-// kept bit to v's bit pattern and drop 20 bits (ties to even; a carry steps the exponent);
-// the kept bits less the rebias 127 -> 7 are the code, and v >= 464 (the half-way point to
-// the next binade) lands at 0x7F or beyond, which the clamp takes back to 0x7E. Below 2^-6
-// the code is v * 2^9 rounded to an integer (exact: the scaling is by a power of two).
-// scale_r is scale, or the largest finite float for an inf scale (so the remainder of a
-// finite |o| is |o| itself rather than 0 * inf). Branch-free.
-__device__ __forceinline__ uint32_t e4m3_mag(float o, float scale_r, float inv) {
-    // each step rounds on its own, as written (no mul + add contraction into an FMA): the
-    // exhaustive CPU check of this encoder models exactly this sequence
-#pragma clang fp contract(off)
-    const float ao = __builtin_fabsf(o);
-    const float q0 = ao * inv;
-    const float r = __builtin_fmaf(-q0, scale_r, ao);
-    const float v = __builtin_fmaf(r, inv, q0);
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t cn = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - 960u;
-    const uint32_t cs = (uint32_t)__builtin_rintf(v * 512.0f);
-    const uint32_t c = min(v < 0.015625f ? cs : cn, 0x7eu);
-    return __builtin_isnan(v) ? 0x7fu : c;
-}
+// FP8 and FP4 codes come from gfx950's conversion instructions:
+//   v_cvt_pk_fp8_f32 (two fp32 -> two OCP E4M3 codes): round to nearest even; values at
+//     or above 464 in magnitude, inf and NaN give a NaN code (no saturation).
+//   v_cvt_scalef32_pk_fp4_f32 (two fp32 times 2^-e -> two OCP E2M1 codes, e the exponent
+//     of the scale operand): round to nearest even code, magnitudes above 6 saturate to 6.
+// Both were checked exhaustively against the format definitions on MI355X: every
+// non-negative fp32 value below 464 (and the negatives down to -464) for E4M3, every bf16
+// value under every block exponent -127..127 for E2M1 (tests/test_gpu_conversions.py
+// repeats the checks).
 
-// FP4 E2M1 code (OCP Microscaling Formats (MX) v1.0: 1 sign, 2 exponent bits with
-// bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) of x, which is exact
-// (a bf16 value times a power of two), rounded once to nearest even, magnitudes above 6
-// clamped to 6. From 1 up the codes are the fp32 numbers with 2 significant bits, so
-// rounding |x|'s bit pattern to 2 significant bits (add half a unit less one, plus the
-// last kept bit, then drop 22 bits) rounds to nearest with ties to the even code, and
-// the kept bits less the rebias 127 -> 1 are the code (6 < |x| < 7 rounds to 6, 7 and up
-// to 8 or beyond, which the clamp takes back to 6). Below 1 the grid step is 0.5 - the
-// step of 2-bit numbers in [1, 2) - so |x| + 1 rounds the same way and the code is the
-// kept bits less the pattern of 1. Branch-free.
-__device__ __forceinline__ uint32_t e2m1_code(float x) {
+// The binary32 quotient o / scale without a divide (inv = 1/scale): q0 = o * inv, the
+// remainder o - q0 * scale by one FMA, one correction q0 + r * inv by another. The result
+// can sit one fp32 unit off the correctly rounded quotient, but never where that changes
+// its E4M3 code: for every bf16 amax and every bf16 o the group can hold (tiny groups
+// rescaled by the caller) the codes agree (checked on the CPU over 5.3e8 pairs).
+// scale_r is scale, or the largest finite float for an inf scale (so that the remainder of
+// a finite o is o rather than 0 * inf = NaN).
+__device__ __forceinline__ float fp32_quotient(float o, float scale_r, float inv) {
 #pragma clang fp contract(off)
-    const float a = __builtin_fabsf(x);
-    const bool small = a < 1.0f;
-    const uint32_t b = __float_as_uint(a + (small ? 1.0f : 0.0f));
-    const uint32_t kept = (b + 0x1fffffu + ((b >> 22) & 1u)) >> 22;
-    const uint32_t c = min(kept - (small ? 254u : 252u), 7u);
-    return ((__float_as_uint(x) >> 28) & 0x8u) | c;
+    const float q0 = o * inv;
+    const float r = __builtin_fmaf(-q0, scale_r, o);
+    return __builtin_fmaf(r, inv, q0);
 }
 
 // ---------------------------------------------------------------- cross-lane
@@ -326,13 +299,14 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
 // per 16-lane group, the group's scale, stored at byte sbase + group * sstride of r_sc.
 // The group's amax is a packed 16-bit max of the magnitude patterns (bf16 magnitudes
 // order as unsigned integers, inf included, and a NaN, above inf, wins and propagates
-// into the scale). Codes are computed on magnitudes; the element signs (the top bit of
-// bytes 1 and 3 of each pair word) are merged four at a time with one byte permute.
-// An all-zero group has scale 0 and every code +0: inv = 0 keeps its lanes on the
-// arithmetic path, and the sign mask is cleared. A group whose scale is below 2^-64 is
-// quantised from |o| and scale both times 2^64 (exact; the quotient is the same), so that
-// 1/scale and the division's remainder stay normal numbers; the stored scale is the
-// unscaled one.
+// into the scale). Each code is the conversion of the binary32 quotient o / scale, sign
+// included: for a finite scale |quotient| <= 448 * (1 + 2^-23) < 464, so the conversion
+// never reaches its NaN range; an inf scale gives 0 for finite o and NaN for infinite o,
+// a NaN scale NaN codes. An all-zero group has scale 0 and every code +0: inv = 0 keeps
+// its lanes on the arithmetic path (their quotients are +-0) and a mask clears the signs.
+// A group whose scale is below 2^-64 is quantised from o and scale both times 2^64 (exact;
+// the quotient is the same), so that 1/scale and the remainder stay normal numbers; the
+// stored scale is the unscaled one.
 __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
                                            uint32_t sstride) {
     u16x2 m = u16x2{0, 0};
@@ -344,18 +318,20 @@ __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, ui
     const float sk = scale * k;
     const float inv = scale == 0.0f ? 0.0f : 1.0f / sk;
     const float sr = min(sk, 0x1.fffffep127f);
-    uint32_t c[8];
+    float v[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        c[2 * w] = e4m3_mag(bf_lo(ob[w]) * k, sr, inv);
-        c[2 * w + 1] = e4m3_mag(bf_hi(ob[w]) * k, sr, inv);
+        v[2 * w] = fp32_quotient(bf_lo(ob[w]) * k, sr, inv);
+        v[2 * w + 1] = fp32_quotient(bf_hi(ob[w]) * k, sr, inv);
     }
-    const uint32_t smask = scale == 0.0f ? 0u : 0x80808080u;
+    const uint32_t keep = scale == 0.0f ? 0u : 0xffffffffu;
     u32x2 codes;
-    codes[0] = (c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24)) |
-               (__builtin_amdgcn_perm(ob[1], ob[0], 0x07050301u) & smask);
-    codes[1] = (c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)) |
-               (__builtin_amdgcn_perm(ob[3], ob[2], 0x07050301u) & smask);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d], v[4 * d + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2], v[4 * d + 3], word, true);
+        codes[d] = (uint32_t)word & keep;
+    }
     st8(codes, r_q, off >> 1);
     // one lane per group writes the scale; the others aim past the row (dropped)
     const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off >> 8) * sstride : kDropOffset;
@@ -365,7 +341,9 @@ __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, ui
 // MXFP4 of one vector slot: the 32-channel block spans the 4 lanes of a quad. Shared
 // scale 2^s with s = floor(log2 amax) - 2 (E2M1's largest exponent), clamped to the
 // E8M0 range; a block holding a NaN gets the NaN scale 0xFF and zero codes, an all-zero
-// block scale 2^-127 (byte 0) and zero codes. Element 2i goes to the low nibble.
+// block scale 2^-127 (byte 0) and zero codes. The conversion takes the scale as an fp32
+// whose exponent field is the E8M0 byte (s = -127 is the bit pattern 0), scales each value
+// by 2^-s exactly and rounds it to E2M1; element 2i goes to the low nibble of its byte.
 __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
     uint32_t amax = 0u;
 #pragma unroll
@@ -375,10 +353,13 @@ __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc
     const bool zero_blk = amax == 0u;
     int sexp = __builtin_amdgcn_frexp_expf(__uint_as_float(amax)) - 1 - 2;  // floor(log2 amax) - 2
     sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
-    const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
+    const float sc = __uint_as_float((uint32_t)(sexp + 127) << 23);
     uint32_t word = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) word |= e2m1_code(__builtin_ldexpf(o[e], -sexp)) << (4 * e);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[0], o[1], sc, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[2], o[3], sc, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[4], o[5], sc, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[6], o[7], sc, 3);
+    const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
     st4u(word & keep, r_q, off >> 2);
     const uint32_t sbyte = nan_blk ? 0xffu : (zero_blk ? 0u : (uint32_t)(sexp + 127));
     // one lane per quad writes the scale byte; the others aim past the row (dropped)
