@@ -233,9 +233,61 @@ def cpu_baseline(d, cfg, quant, emit_out, budget_s):
         spent += time.perf_counter() - t0
         passes += 1
     gbps = nbytes(cfg, quant, emit_out) * passes / spent / 1e9
+    # one thread on a sample of rows, for the per-core figure
+    rows = min(cfg.T, 256)
+    P1, r1 = d["partials"][:, :rows], d["residual"][:rows]
+    t0 = time.perf_counter()
+    if quant == "mxfp4":
+        oracle.reduce_add_rmsnorm_mxfp4(P1, r1, d["gamma"], 1e-6, emit_out, nthreads=1)
+    elif quant:
+        oracle.reduce_add_rmsnorm_quant_group(P1, r1, d["gamma"], 1e-6, 128, emit_out, nthreads=1)
+    else:
+        oracle.reduce_add_rmsnorm(P1, r1, d["gamma"], 1e-6, nthreads=1)
+    one = time.perf_counter() - t0
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} full pass(es) over the workload ({cfg.T} rows), {spent:.1f} s",
-            "ms_per_call": round(spent / passes * 1e3, 2)}
+            "ms_per_call": round(spent / passes * 1e3, 2),
+            "one_thread": {"GBps": round(nbytes(cfg, quant, emit_out) * rows / cfg.T / one / 1e9, 3),
+                           "sample": f"{rows} rows, {one:.2f} s"},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_ceiling(dev, reps=5):
+    """Streaming references beside the published peak, each moving 1 GiB in and 1 GiB out and
+    timed with events (median of reps): torch's device copy, and this library's all-reduce of a
+    single rank (farn_reduce with R = 1: a bf16 copy through the kernels' own access pattern)."""
+    def median_time(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            fn()
+            end.record()
+            torch.cuda.synchronize()
+            times.append(start.elapsed_time(end) * 1e-3)
+        return statistics.median(times)
+    src = torch.empty((1 << 16, 1 << 13), dtype=torch.bfloat16, device=dev)   # 1 GiB
+    src.view(torch.int16).random_(-0x4000, 0x4000)                            # finite bf16 patterns
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn in (("torch_copy", lambda: dst.copy_(src)), ("farn_reduce_R1", lambda: F.reduce([src], out=dst))):
+        gbps = 2 * (1 << 30) / median_time(fn) / 1e9
+        out[name] = {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
+    out["what"] = f"1 GiB read + 1 GiB written per call, median of {reps}"
+    return out
 
 
 def recorded_traffic(workload):
@@ -398,6 +450,9 @@ def main():
                      "hbm_bytes_per_launch": traffic},
         "parity": parity,
     }
+    if not args.no_secondary:
+        log("copy ceiling")
+        result["copy_ceiling"] = copy_ceiling(dev)
     if args.cpu_budget > 0:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(d, cfg, quant, emit_out, args.cpu_budget)
