@@ -1,5 +1,5 @@
 // HIP kernels for gfx950 (CDNA4): fused reduce of R rank partials + residual add +
-// RMSNorm (+ per-128-channel E4M3 quant), one token row at a time.
+// RMSNorm (+ per-128-channel E4M3 quant, or MXFP4), one token row at a time.
 //
 // The op is the per-GPU body of the fused tensor-parallel all-reduce + RMSNorm of
 // "ROCm AITER fused all-reduce + RMSNorm" (vLLM #37646 summary: all-reduce, then
@@ -14,8 +14,9 @@
 //   wave is 64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is
 //   exactly 16 consecutive lanes (one DPP row) of one vector slot.
 //   Per lane: the source issues the loads of the row's slots before consuming any (the
-//   compiler may still sink some below the first slot's fold); the partials are summed in fp32 in rank order, the residual added last, the sum
-//   rounded to bf16 (residual_out) and kept packed in registers. The sum of squares
+//   compiler may still sink some below the first slot's fold); the partials are summed
+//   in fp32 in rank order, the residual added last, the sum rounded to bf16
+//   (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
 //   per wave through LDS -> every wave adds the per-wave values in wave order; the
 //   normalisation product is fp64 too, rounded once to bf16. The row never passes
@@ -239,8 +240,7 @@ __device__ __forceinline__ void load_slot(SlotIn<R> &in, const Params &k, int64_
 }
 
 // fp32 sum of the partials in rank order, residual last (skipped, not a +0, when there
-// is none), rounded to bf16 and stored as residual_out; accumulates the squares of the
-// rounded values into ss (fp64). Lanes past the row end see zeros and add nothing.
+// is none), rounded to bf16: four packed pairs. Lanes past the row end see zeros.
 template <int R>
 __device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
     u32x4 packed;
@@ -260,6 +260,8 @@ __device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
     return packed;
 }
 
+// fold_slot, stored as residual_out, with the squares of the rounded values added to ss
+// (fp64; zeros from lanes past the row end add nothing).
 template <int R>
 __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
                                              uint32_t off, double &ss) {
@@ -276,13 +278,12 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
 }
 
 // Row statistics in fp64: wave DPP tree, one double per wave through `slot` (kMaxWaves
-// doubles), then every wave adds the per-wave values in wave order; rstd =
-// 1/sqrt(ss/H + eps) with correctly rounded fp64 division and square root. The
-// kernel is HBM-bound with ample ALU to spare, and fp64 statistics put `out` on the
-// bf16 value the exact statistics give (an fp32 tree moves about one element in 10^4
-// by one bf16 step, and when that element is a group's amax its scale moves by up to
-// 2^-7). Callers alternate two slots between consecutive rows, so one barrier per row
-// suffices.
+// doubles), one barrier, then every wave adds the per-wave values in wave order; rstd =
+// 1/sqrt(ss/H + eps) with correctly rounded fp64 division and square root. fp64
+// statistics put `out` on the bf16 value the exact statistics give (an fp32 tree moves
+// about one element in 10^4 by one bf16 step, and when that element is a group's amax
+// its scale moves by up to 2^-7); MI355X runs fp64 vector FMAs at the rate of unpacked
+// fp32 ones.
 __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *slot) {
     const int lane = (int)threadIdx.x & 63;
     const int wave = (int)threadIdx.x >> 6;
@@ -311,8 +312,10 @@ __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, ui
                                            uint32_t sstride) {
     u16x2 m = u16x2{0, 0};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[w] & 0x7fff7fffu));
-    const uint32_t amax = row16_umax(max((uint32_t)m[0], (uint32_t)m[1])) << 16;  // 16 lanes = 128 channels
+    for (int w = 0; w < 4; ++w)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[w] & 0x7fff7fffu));
+    // 16 lanes = one 128-channel group
+    const uint32_t amax = row16_umax(max((uint32_t)m[0], (uint32_t)m[1])) << 16;
     const float scale = __uint_as_float(amax) / 448.0f;  // correctly rounded
     const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
     const float sk = scale * k;
@@ -480,7 +483,8 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) xv[v] = ld16(r_x, (v * blockDim.x + threadIdx.x) * 16u);
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) quant_slot(xv[v], r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
+    for (int v = 0; v < VPL; ++v)
+        quant_slot(xv[v], r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
 }
 
 // ---------------------------------------------------------------- dispatch tables
