@@ -497,6 +497,36 @@ def test_random_shapes(dev):
             run_mxfp4(u, variant, emit_out=bool(i % 2), label=f"rand{i}")
 
 
+def test_two_streams_at_once(dev):
+    """The library keeps no state: calls enqueued on two streams at the same time, on different
+    inputs (one FP8, one plain, one MXFP4 per stream, back to back), each match the oracle."""
+    cases = []
+    for i, (T, H) in enumerate([(96, 7168), (40, 4096)]):
+        d = make_inputs(CONFIGS["tiny"], seed=80 + i, R=4 + 4 * i, T=T, H=H)
+        cases.append((d, Uploaded(d, dev)))
+    torch.cuda.synchronize()  # inputs were uploaded on the default stream
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    say("[gpu] two streams at once")
+    outs = []
+    for (d, u), st in zip(cases, streams):
+        with torch.cuda.stream(st):
+            fp8 = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS)
+            plain = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS)
+            mx = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS)
+        outs.append((fp8, plain, mx))
+    torch.cuda.synchronize()
+    for (d, u), (fp8, plain, mx) in zip(cases, outs):
+        rows = np.arange(u.T)
+        r_ro, r_out, r_q, r_s = u.oracle_rows(rows, True)
+        assert np.array_equal(from_dev_bf16(fp8[0]), r_ro) and np.array_equal(from_dev_bf16(fp8[1]), r_out)
+        rep = compare_fp8(fp8[2].cpu().numpy(), r_q, fp8[3].cpu().numpy(), r_s)
+        assert rep["n_code_diff"] == 0 and rep["max_scale_rel_err"] == 0.0, rep
+        assert np.array_equal(from_dev_bf16(plain[0]), r_ro) and np.array_equal(from_dev_bf16(plain[1]), r_out)
+        m_ro, m_out, m_q, m_s = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS,
+                                                              True, nthreads=8)
+        assert np.array_equal(mx[2].cpu().numpy(), m_q) and np.array_equal(mx[3].cpu().numpy(), m_s)
+
+
 def test_plain_c_client():
     """tests/c_abi_client.c: a C program with no Python and no torch calls the ABI on
     hipMalloc'd memory and checks closed-form results (exit status 0 = all hold)."""
