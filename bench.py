@@ -10,8 +10,8 @@ Infinity Cache, so every call streams from HBM.
 
 Prints ONE JSON line: value = algorithmic bytes per step / time per step (GB/s), with
 the roofline of the kernel (HBM bound, 8 TB/s peak), the CPU oracle timed on host
-cores on the same workload, a parity gate against the oracle on sampled rows, and
-secondary figures for the decode shapes (us/call).
+cores on the same workload (its last pass also checks every output of the timed GPU
+call: the parity field), and secondary figures for the decode shapes (us/call).
 """
 
 from __future__ import annotations
@@ -183,30 +183,24 @@ def median_graph(sets, variant, calls, replays, method="call", runs=3):
     return statistics.median(time_graph(sets, variant, calls, replays, method) for _ in range(runs))
 
 
-def parity_gate(d, bufs, quant, emit_out, rows):
-    import oracle
+def parity_report(ref, bufs, quant, emit_out):
+    """GPU outputs of the timed call against reference outputs `ref` = (residual_out, out,
+    q, scales) as the oracle returns them, over every row."""
     from tests.parity import compare_bf16, compare_fp8, from_dev_bf16, within_tolerance
-    P = d["partials"][:, rows, :]
-    res = d["residual"][rows]
+    r_ro, r_out = ref[0], ref[1]
+    mx = fp8 = None
     if quant == "mxfp4":
         from tests.parity import compare_mxfp4, mxfp4_within_tolerance
-        r_ro, r_out, r_q, r_s = oracle.reduce_add_rmsnorm_mxfp4(P, res, d["gamma"], 1e-6, emit_out, nthreads=8)
-        mx = compare_mxfp4(bufs.q.cpu().numpy()[rows], r_q, bufs.s.cpu().numpy()[rows], r_s)
-        fp8 = None
+        mx = compare_mxfp4(bufs.q.cpu().numpy(), ref[2], bufs.s.cpu().numpy(), ref[3])
     elif quant:
-        r_ro, r_out, r_q, r_s = oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], 1e-6, 128,
-                                                                      emit_out, nthreads=8)
-        fp8 = compare_fp8(bufs.q.cpu().numpy()[rows], r_q, bufs.s.cpu().numpy()[rows], r_s)
-    else:
-        r_ro, r_out = oracle.reduce_add_rmsnorm(P, res, d["gamma"], 1e-6, nthreads=8)
-        fp8 = None
-    rep_ro = compare_bf16("residual_out", from_dev_bf16(bufs.ro)[rows], r_ro)
-    rep_out = compare_bf16("out", from_dev_bf16(bufs.out)[rows], r_out) if bufs.out is not None else None
+        fp8 = compare_fp8(bufs.q.cpu().numpy(), ref[2], bufs.s.cpu().numpy(), ref[3])
+    rep_ro = compare_bf16("residual_out", from_dev_bf16(bufs.ro), r_ro)
+    rep_out = compare_bf16("out", from_dev_bf16(bufs.out), r_out) if bufs.out is not None else None
     ok, why = within_tolerance(rep_ro, rep_out, fp8)
-    if quant == "mxfp4":
+    if mx is not None:
         ok2, why2 = mxfp4_within_tolerance(mx)
         ok, why = ok and ok2, "; ".join(w for w in (why, why2) if w)
-    return {"ok": ok, "why": why, "rows_checked": int(len(rows)),
+    return {"ok": ok, "why": why, "rows_checked": int(bufs.T), "against": "oracle, all rows",
             "residual_out_bit_diffs": rep_ro["n_bit_diff"],
             "out_max_rel_err": None if rep_out is None else rep_out["max_rel_err"],
             "out_bit_diffs": None if rep_out is None else rep_out["n_bit_diff"],
@@ -214,22 +208,24 @@ def parity_gate(d, bufs, quant, emit_out, rows):
             "scale_max_rel_err": None if fp8 is None else fp8["max_scale_rel_err"]}
 
 
-def cpu_baseline(d, cfg, quant, emit_out, budget_s):
+def cpu_baseline(d, cfg, quant, emit_out, budget_s, bufs=None):
     """The oracle as it stands, on the host cores, over whole passes of the workload until
-    about budget_s seconds have been spent."""
+    about budget_s seconds have been spent. With `bufs` (the timed GPU call's buffers), the
+    last pass's outputs are also compared with the GPU's over every row: returns
+    (baseline, parity report or None)."""
     import oracle
     threads = min(16, len(os.sched_getaffinity(0)))
-    passes, spent = 0, 0.0
+    passes, spent, ref = 0, 0.0, None
     while spent < budget_s:
         t0 = time.perf_counter()
         if quant == "mxfp4":
-            oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], 1e-6, emit_out,
-                                            nthreads=threads)
+            ref = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], 1e-6, emit_out,
+                                                  nthreads=threads)
         elif quant:
-            oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], 1e-6, 128,
-                                                  emit_out, nthreads=threads)
+            ref = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], 1e-6, 128,
+                                                        emit_out, nthreads=threads)
         else:
-            oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], 1e-6, nthreads=threads)
+            ref = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], 1e-6, nthreads=threads)
         spent += time.perf_counter() - t0
         passes += 1
     gbps = nbytes(cfg, quant, emit_out) * passes / spent / 1e9
@@ -249,7 +245,7 @@ def cpu_baseline(d, cfg, quant, emit_out, budget_s):
             "ms_per_call": round(spent / passes * 1e3, 2),
             "one_thread": {"GBps": round(nbytes(cfg, quant, emit_out) * rows / cfg.T / one / 1e9, 3),
                            "sample": f"{rows} rows, {one:.2f} s"},
-            "cpu_model": cpu_model()}
+            "cpu_model": cpu_model()}, (None if bufs is None else parity_report(ref, bufs, quant, emit_out))
 
 
 def cpu_model():
@@ -396,18 +392,6 @@ def main():
     bufs = Bufs(d, dev, quant, emit_out)
     nb = nbytes(cfg, quant, emit_out)
 
-    parity = None
-    if not args.no_parity:
-        bufs.call(variant)
-        torch.cuda.synchronize()
-        rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 32)]))
-        parity = parity_gate(d, bufs, quant, emit_out, rows)
-        log(f"parity: {parity}")
-        if not parity["ok"]:
-            print(json.dumps({"metric": METRIC, "error": "parity gate failed", "parity": parity}))
-            sys.exit(1)
-
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -448,14 +432,19 @@ def main():
                      "kernel": "farn_rows (" + {1: "latency", 2: "bandwidth"}[ran] + " shape)",
                      "algorithmic_bytes_per_launch": nb,
                      "hbm_bytes_per_launch": traffic},
-        "parity": parity,
+        "parity": None,
     }
     if not args.no_secondary:
         log("copy ceiling")
         result["copy_ceiling"] = copy_ceiling(dev)
     if args.cpu_budget > 0:
-        log("timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(d, cfg, quant, emit_out, args.cpu_budget)
+        log("timing the CPU oracle (its last pass also checks the timed call's outputs)")
+        result["cpu_baseline"], result["parity"] = cpu_baseline(
+            d, cfg, quant, emit_out, args.cpu_budget, None if args.no_parity else bufs)
+        log(f"parity: {result['parity']}")
+        if result["parity"] is not None and not result["parity"]["ok"]:
+            print(json.dumps({"metric": METRIC, "error": "parity check failed", "parity": result["parity"]}))
+            sys.exit(1)
     if not args.no_secondary:
         del bufs
         torch.cuda.empty_cache()
