@@ -67,6 +67,11 @@ def test_status_strings_and_select():
     assert F.select_variant(8, 4096, 2048, False) == F.VARIANT_LATENCY
     assert F.select_variant(8, 8192, 2048, False) == F.VARIANT_BANDWIDTH
     assert F.select_variant(8, 8192, 1024, False) == F.VARIANT_LATENCY  # one wave per row
+    assert F.select_variant(8, 1024, 5120, True) == F.VARIANT_BANDWIDTH  # the H = 5120 band
+    assert F.select_variant(8, 2048, 5120, True) == F.VARIANT_LATENCY
+    assert F.select_variant(2, 8192, 4096, True) == F.VARIANT_BANDWIDTH  # two ranks
+    assert F.select_variant(4, 8192, 4096, True) == F.VARIANT_LATENCY
+    assert F.select_variant(2, 64, 4096, False) == F.VARIANT_LATENCY
 
 
 class FakeCall:
