@@ -56,7 +56,7 @@ extern "C" {
 typedef enum farn_status {
     FARN_OK = 0,
     FARN_ERR_NULL = 1,    /* a required pointer is NULL */
-    FARN_ERR_SHAPE = 2,   /* R not in [1, FARN_MAX_R]; T < 0; H <= 0, H % 8 != 0 or
+    FARN_ERR_SHAPE = 2,   /* R not in [1, FARN_MAX_R]; T < 0 or T > 2^40; H <= 0, H % 8 != 0 or
                              H > FARN_MAX_H; FP8 quant: group_size != 128 or H % 128 != 0;
                              MXFP4: H % 32 != 0 */
     FARN_ERR_ALIGN = 3,   /* a bf16 / q buffer is not 16-byte aligned, or scales not 4-byte aligned */

@@ -146,7 +146,6 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
                            residual_out, out, q, scales);
     if (st != FARN_OK || T == 0) return st;
     const int shape = variant == FARN_VARIANT_AUTO ? select(R, T, H, quant != kNone ? 1 : 0) : variant;
-    if (T > INT32_MAX) return FARN_ERR_SHAPE;  // one workgroup per row
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
     c.R = R;
@@ -224,7 +223,6 @@ farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H
                         void *stream) {
     farn_status st = check_reduce(partials, R, T, H, out);
     if (st != FARN_OK || T == 0) return st;
-    if (T > INT32_MAX) return FARN_ERR_SHAPE;
     farn::Call c = blank_call(stream);
     c.kind = farn::Kind::kReduce;
     for (int r = 0; r < R; ++r) c.partials[r] = partials[r];
@@ -239,7 +237,6 @@ farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size
                              float *scales, void *stream) {
     farn_status st = check_quant(x, T, H, group_size, q, scales);
     if (st != FARN_OK || T == 0) return st;
-    if (T > INT32_MAX) return FARN_ERR_SHAPE;
     farn::Call c = blank_call(stream);
     c.kind = farn::Kind::kQuant;
     c.T = T;

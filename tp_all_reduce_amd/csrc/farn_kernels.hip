@@ -8,7 +8,8 @@
 // quant of the bf16 normalised output). Here the R partial buffers sit in local HBM.
 //
 // Work mapping:
-//   One workgroup per token row, grid = T. A row of H bf16 is NV = H/8 16-byte vectors,
+//   One workgroup per token row, grid = T (in several launches of consecutive rows when
+//   T x L exceeds a dispatch's 2^32 - 1 work-items). A row of H bf16 is NV = H/8 16-byte vectors,
 //   spread over L lanes (a multiple of 64, <= 1024) with VPL vectors per lane,
 //   lane-strided: lane l holds vectors l, l+L, l+2L, ... So every load instruction of a
 //   wave is 64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is
@@ -58,6 +59,7 @@ struct Params {
     const void *x;      // bf16 [T,H] input of the standalone quant kernel
     int scale_cols;     // FP8 scales column-major [H/128, T] (else row-major [T, H/128])
     int64_t T;
+    int64_t t0;         // row of this launch's first workgroup
     int nvec;           // H / 8
     int ngroups;        // H / 128
     double h;           // H (mean divisor)
@@ -447,7 +449,7 @@ __device__ __forceinline__ void load_gamma(u32x4 (&gam)[VPL], const Params &k) {
 template <int R, int VPL, int QM>
 __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     __shared__ double slot[kMaxWaves];
-    const int64_t t = blockIdx.x;
+    const int64_t t = k.t0 + blockIdx.x;
     SlotIn<R> in;
     load_slot<R>(in, k, t, threadIdx.x * 16u);
     u32x4 gam[VPL];
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
 // arithmetic as the fused kernel's corresponding steps.
 template <int R, int VPL>
 __global__ __launch_bounds__(1024) void farn_reduce_rows(const Params k) {
-    const int64_t t = blockIdx.x;
+    const int64_t t = k.t0 + blockIdx.x;
     const int rb = k.nvec * 16;
     const rsrc_t r_out = row_rsrc(k.res_out, t * (int64_t)rb, rb);
 #pragma unroll
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(1024) void farn_reduce_rows(const Params k) {
 
 template <int VPL>
 __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
-    const int64_t t = blockIdx.x;
+    const int64_t t = k.t0 + blockIdx.x;
     const int rb = k.nvec * 16;
     const rsrc_t r_x = row_rsrc(k.x, t * (int64_t)rb, rb);
     const rsrc_t r_q = row_rsrc(k.q, t * (int64_t)k.nvec * 8, k.nvec * 8);
@@ -541,6 +543,7 @@ static Params make_params(const Call &c) {
     k.x = c.x;
     k.scale_cols = c.scale_cols ? 1 : 0;
     k.T = c.T;
+    k.t0 = 0;
     k.nvec = (int)(c.H / 8);
     k.ngroups = (int)(c.H / 128);
     k.h = (double)c.H;
@@ -562,9 +565,17 @@ int launch(const Call &c, int variant) {
     }
     if (!fn) return 1;
 
-    const Params k = make_params(c);
-    hipLaunchKernelGGL(fn, dim3((uint32_t)c.T), dim3((uint32_t)rs.lanes), 0, (hipStream_t)c.stream, k);
-    return hipGetLastError() == hipSuccess ? 0 : 1;
+    // A dispatch holds at most 2^32 - 1 work-items: very tall arrays go out as several
+    // launches of consecutive rows (rows are independent).
+    const int64_t max_rows = (int64_t)(UINT32_MAX / (uint32_t)rs.lanes);
+    Params k = make_params(c);
+    for (int64_t t0 = 0; t0 < c.T; t0 += max_rows) {
+        k.t0 = t0;
+        const int64_t n = c.T - t0 < max_rows ? c.T - t0 : max_rows;
+        hipLaunchKernelGGL(fn, dim3((uint32_t)n), dim3((uint32_t)rs.lanes), 0, (hipStream_t)c.stream, k);
+        if (hipGetLastError() != hipSuccess) return 1;
+    }
+    return 0;
 }
 
 }  // namespace farn
