@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import tp_all_reduce_amd as F  # noqa: E402  (raises if the HIP library is not built)
-from gen import CONFIGS, make_inputs, sweep_config  # noqa: E402
+from gen import CONFIGS, SWEEP_T, make_inputs, sweep_config  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
 METRIC = "effective HBM GB/s (% of MI355X peak) and µs/call of fused reduce+RMSNorm"
@@ -48,7 +48,7 @@ WORKLOADS = {
     "prefill_mxfp4": (CONFIGS["prefill"], "mxfp4", True),
     "decode_ds_mxfp4": (CONFIGS["decode_ds"], "mxfp4", True),
 }
-for _T in (2 ** k for k in range(1, 13)):
+for _T in SWEEP_T:
     WORKLOADS[f"sweep_T{_T}"] = (sweep_config(_T), False, True)
 
 VARIANT_NAMES = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
@@ -336,6 +336,31 @@ def secondary(dev, steps):
     return out
 
 
+def sweep(dev):
+    """The message-size sweep (R = 8, H = 8192, T = 2 .. 4096, plain call) in us/call by graph
+    replay: hot (one buffer set, cache-resident) and cold (sets rotated over >= 1 GiB, so every
+    call streams from HBM rather than the 256 MB last-level cache), with the cold rate."""
+    out = {}
+    for T in SWEEP_T:
+        cfg = sweep_config(T)
+        b = Bufs(make_inputs(cfg), dev, False, True)
+        nb = nbytes(cfg, False, True)
+        hot = median_graph([b], F.VARIANT_AUTO, 200, 10)
+        k = max(1, -(-(1 << 30) // nb))
+        sets = [b] + [b.clone(dev) for _ in range(k - 1)]
+        calls = k * max(1, 200 // k)
+        cold = median_graph(sets, F.VARIANT_AUTO, calls, max(2, 2000 // calls))
+        gbps = nb / (cold * 1e-3) / 1e9
+        out[f"T{T}"] = {"us_per_call_graph_hot": round(hot * 1e3, 2), "us_per_call_graph_cold": round(cold * 1e3, 2),
+                        "GBps_graph_cold": round(gbps, 1), "pct_of_peak_cold": round(100 * gbps / PEAK_HBM_GBPS, 1),
+                        "rotation_sets": k, "bytes_per_call": nb,
+                        "variant": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)]}
+        log(f"sweep T={T}: {out[f'T{T}']}")
+        del sets, b
+        torch.cuda.empty_cache()
+    return out
+
+
 def unfused(dev):
     """What fusion buys: the FP8 step as one kernel (fused), two (fused AR+RMSNorm, then quant)
     and three (all-reduce, add+RMSNorm, quant), as the sglang benchmark compares them. Prefill:
@@ -372,6 +397,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the message-size sweep (R=8, H=8192, T=2..4096), hot and cache-cold")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one torch copy of 1 GiB (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -452,6 +479,9 @@ def main():
         result["secondary"] = secondary(dev, 200)
         log("unfused compositions")
         result["secondary"]["unfused_fp8"] = unfused(dev)
+    if args.sweep:
+        log("message-size sweep")
+        result.setdefault("secondary", {})["sweep_R8_H8192"] = sweep(dev)
     print(json.dumps(result), flush=True)
 
 

@@ -5,4 +5,4 @@ bench. It draws random numbers and rounds them to bf16 with torch's own cast;
 it holds none of the op's arithmetic.
 """
 
-from .inputs import CONFIGS, Config, make_inputs, sweep_config  # noqa: F401
+from .inputs import CONFIGS, SWEEP_T, Config, make_inputs, sweep_config  # noqa: F401
