@@ -178,8 +178,8 @@ def time_graph(sets, variant, calls, replays, method="call"):
 
 def median_graph(sets, variant, calls, replays, method="call", runs=3):
     """Median of `runs` time_graph measurements: decode calls are bound by instruction
-    issue on a few compute units and move with the shader clock from one measurement to
-    the next, by up to 15 %."""
+    issue and memory latency on a few compute units and move with the shader clock from one
+    measurement to the next, by up to 15 %."""
     return statistics.median(time_graph(sets, variant, calls, replays, method) for _ in range(runs))
 
 

@@ -16,9 +16,11 @@ binary32 quotient out/scale (numpy's IEEE single division).
 
 from __future__ import annotations
 
+import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 import oracle
 
@@ -100,6 +102,14 @@ def _check_groups(amax_patterns: np.ndarray) -> int:
 def test_quotient_codes():
     """Every finite bf16 value each group can hold, for ~3,300 group maxima: about 10^8 pairs."""
     assert _check_groups(_amax_patterns(3000, seed=1)) > 100_000_000
+
+
+def test_quotient_codes_every_amax():
+    """Opt-in (FARN_MODEL_EVERY_AMAX=1, a few minutes): every finite nonzero bf16 magnitude as
+    the group maximum, with every bf16 value the group can hold: about 1.07e9 pairs."""
+    if not os.environ.get("FARN_MODEL_EVERY_AMAX"):
+        pytest.skip("set FARN_MODEL_EVERY_AMAX=1 to check every bf16 group maximum (a few minutes)")
+    assert _check_groups(np.arange(0x0001, 0x7F80, dtype=np.uint32)) > 1_000_000_000
 
 
 def test_quotient_model_specials():
