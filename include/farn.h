@@ -42,7 +42,9 @@
  * non-OK status means no work was enqueued (the analogue of the pages' "None,
  * caller falls back"). T == 0 returns FARN_OK and enqueues nothing; the [T,H]
  * buffers may then be NULL (gamma and the partials array may not).
- * FARN_ERR_LAUNCH is returned when the launch itself fails.
+ * FARN_ERR_LAUNCH is returned when a kernel launch itself fails. A call whose
+ * rows need more than one launch (T x lanes above 2^32 - 1 work-items, e.g.
+ * T >= 4,194,304 at H = 8192) may then have enqueued its earlier row chunks.
  */
 #ifndef FARN_H
 #define FARN_H

@@ -569,12 +569,16 @@ int launch(const Call &c, int variant) {
     // A dispatch holds at most 2^32 - 1 work-items: very tall arrays go out as several
     // launches of consecutive rows (rows are independent).
     const int64_t max_rows = (int64_t)(UINT32_MAX / (uint32_t)rs.lanes);
+    // hipLaunchKernel returns this launch's own status (hipGetLastError would also report,
+    // and clear, an earlier error of the caller's).
     Params k = make_params(c);
+    void *args[] = {&k};
     for (int64_t t0 = 0; t0 < c.T; t0 += max_rows) {
         k.t0 = t0;
         const int64_t n = c.T - t0 < max_rows ? c.T - t0 : max_rows;
-        hipLaunchKernelGGL(fn, dim3((uint32_t)n), dim3((uint32_t)rs.lanes), 0, (hipStream_t)c.stream, k);
-        if (hipGetLastError() != hipSuccess) return 1;
+        if (hipLaunchKernel((const void *)fn, dim3((uint32_t)n), dim3((uint32_t)rs.lanes), args, 0,
+                            (hipStream_t)c.stream) != hipSuccess)
+            return 1;
     }
     return 0;
 }
