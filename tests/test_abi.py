@@ -254,6 +254,22 @@ def test_option_bits():
     assert p.call() == VARIANT
 
 
+def test_column_major_scales_limit():
+    """Column-major FP8 scales are addressed through one 32-bit range: T * H/128 * 4 bytes
+    must stay below 2^31. At H = 32768 that is T < 2^21. Arrays are spaced 2^40 bytes apart,
+    so the ranges do not overlap."""
+    def tall(T):
+        c = FakeCall(R=1, T=T, H=32768, quant=True)
+        c.partials = [1 << 41]
+        c.residual, c.gamma, c.residual_out = 2 << 41, 3 << 41, 4 << 41
+        c.out, c.q, c.scales = 5 << 41, 6 << 41, 7 << 41
+        c.variant = 0x100
+        return c
+    # (a call that passed every check would launch on these fake addresses: none is made)
+    assert tall(1 << 21).call() == SHAPE
+    assert tall(1 << 62).call() == SHAPE  # rejected by the T range check, no overflow
+
+
 def test_bench_refuses_several_gpus():
     """bench.py measures one GPU; asked for more it exits with a message before touching a GPU."""
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -140,11 +140,12 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     if ((options & ~(0xff | FARN_SCALES_COL_MAJOR)) != 0) return FARN_ERR_VARIANT;
     if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH) return FARN_ERR_VARIANT;
     if (cols && quant != kFp8) return FARN_ERR_VARIANT;
-    // column-major scales are addressed through one 32-bit buffer range
-    if (cols && T * (H / FARN_GROUP) * 4 >= ((int64_t)1 << 31)) return FARN_ERR_SHAPE;
     farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
                            residual_out, out, q, scales);
     if (st != FARN_OK || T == 0) return st;
+    // column-major scales are addressed through one 32-bit buffer range (T and H are in
+    // range here, so the product cannot overflow)
+    if (cols && T * (H / FARN_GROUP) * 4 >= ((int64_t)1 << 31)) return FARN_ERR_SHAPE;
     const int shape = variant == FARN_VARIANT_AUTO ? select(R, T, H, quant != kNone ? 1 : 0) : variant;
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
