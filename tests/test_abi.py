@@ -290,3 +290,16 @@ def test_c_client_builds_against_header_alone(tmp_path):
                     f"-L{os.path.dirname(F.LIB_PATH)}", "-lfarn", f"-L{rocm}/lib", "-lamdhip64"],
                    check=True)
     assert os.path.getsize(exe) > 0
+
+
+def test_binding_refuses_host_tensors():
+    """The library takes plain pointers and cannot tell host memory from device memory: the
+    binding refuses host tensors before calling it."""
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    g = torch.ones(256, dtype=torch.bfloat16)
+    calls = [lambda: F.reduce_add_rmsnorm([x], None, g), lambda: F.reduce_add_rmsnorm_quant_group([x], None, g),
+             lambda: F.reduce_add_rmsnorm_mxfp4([x], None, g), lambda: F.reduce([x]), lambda: F.quant_group(x)]
+    for call in calls:
+        with pytest.raises(ValueError, match="on the GPU"):
+            call()

@@ -541,6 +541,37 @@ def test_plain_c_client():
     assert "0 mismatches" in proc.stdout
 
 
+# ------------------------------------------------------------------ binding checks
+def test_binding_rejects_bad_output_buffers(dev):
+    """Output buffers of the wrong shape, dtype or device are refused by the binding before
+    the library is called (the library only sees pointers)."""
+    T, H = 4, 256
+    P = [torch.zeros(T, H, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    g = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    small = torch.empty(T - 1, H, dtype=torch.bfloat16, device=dev)
+    host = torch.empty(T, H, dtype=torch.bfloat16)
+    bad = [
+        lambda: F.reduce_add_rmsnorm(P, None, g, residual_out=small),
+        lambda: F.reduce_add_rmsnorm(P, None, g, out=host),
+        lambda: F.reduce_add_rmsnorm_quant_group(P, None, g, residual_out=small),
+        lambda: F.reduce_add_rmsnorm_quant_group(P, None, g, out=host),
+        lambda: F.reduce_add_rmsnorm_quant_group(P, None, g, q=torch.empty(T, H, dtype=torch.uint8)),
+        lambda: F.reduce_add_rmsnorm_quant_group(P, None, g, scales=torch.empty(T, dtype=torch.float32, device=dev)),
+        lambda: F.reduce_add_rmsnorm_quant_group(P, None, g, q=torch.empty(T, H, dtype=torch.int32, device=dev)),
+        lambda: F.reduce_add_rmsnorm_mxfp4(P, None, g, residual_out=small),
+        lambda: F.reduce_add_rmsnorm_mxfp4(P, None, g, q=torch.empty(T, H, dtype=torch.uint8, device=dev)),
+        lambda: F.reduce_add_rmsnorm_mxfp4(P, None, g, scales=torch.empty(T, H // 32, dtype=torch.uint8)),
+        lambda: F.reduce(P, out=small),
+        lambda: F.quant_group(P[0], q=torch.empty(T, H - 128, dtype=torch.uint8, device=dev)),
+        lambda: F.quant_group(P[0], scales=torch.empty(T, H // 128, dtype=torch.float32)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(f"case {i} was accepted")
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ rows beyond one dispatch
 def test_rows_beyond_one_dispatch(dev):
     """One workgroup per row, and a dispatch holds at most 2^32 - 1 work-items: at H = 8192 on

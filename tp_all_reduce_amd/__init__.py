@@ -93,6 +93,14 @@ def _ptr_array(ts):
     return arr
 
 
+def _device_of(t, name="partials[0]"):
+    """The GPU the call runs on: that of its first input. The library takes plain pointers and
+    cannot tell host memory from device memory, so host tensors are refused here."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: expected a tensor on the GPU, got one on {t.device}")
+    return t.device
+
+
 def _check_bf16(name, t, shape, device):
     if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
             or t.device != device:
@@ -100,9 +108,24 @@ def _check_bf16(name, t, shape, device):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
+def _check_buf(name, t, dtypes, numel, device):
+    """A code or scale buffer: contiguous, of one of `dtypes`, `numel` elements, on `device`."""
+    if t.dtype not in dtypes or t.numel() != numel or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected a contiguous {' / '.join(str(d) for d in dtypes)} tensor of "
+                         f"{numel} elements on {device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def _stream(device, stream):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _run(device, fn, *args):
+    """Call into the library with `device` current (HIP launches on the current device)."""
+    if device.index is not None and device.index != torch.cuda.current_device():
+        with torch.cuda.device(device):
+            return fn(*args)
+    return fn(*args)
 
 
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual_out=None,
@@ -112,7 +135,7 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
     residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
     p0 = partials[0]
     T, H = p0.shape
-    dev = p0.device
+    dev = _device_of(p0)
     for i, p in enumerate(partials):
         _check_bf16(f"partials[{i}]", p, (T, H), dev)
     if residual is not None:
@@ -122,9 +145,9 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
     out = torch.empty_like(p0) if out is None else out
     _check_bf16("residual_out", residual_out, (T, H), dev)
     _check_bf16("out", out, (T, H), dev)
-    st = _lib.farn_reduce_add_rmsnorm_ex(
-        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
-        _ptr(residual_out), _ptr(out), _stream(dev, stream), variant)
+    st = _run(dev, _lib.farn_reduce_add_rmsnorm_ex,
+              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
+              _ptr(residual_out), _ptr(out), _stream(dev, stream), variant)
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm")
     return residual_out, out
@@ -139,29 +162,30 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
     [H/128, T] with scales_col_major)."""
     p0 = partials[0]
     T, H = p0.shape
-    dev = p0.device
+    dev = _device_of(p0)
     for i, p in enumerate(partials):
         _check_bf16(f"partials[{i}]", p, (T, H), dev)
     if residual is not None:
         _check_bf16("residual", residual, (T, H), dev)
     _check_bf16("gamma", gamma, (H,), dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    _check_bf16("residual_out", residual_out, (T, H), dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
+    if out is not None:
+        _check_bf16("out", out, (T, H), dev)
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
     G = H // group_size if group_size > 0 else 0
     if scales is None:
         scales = torch.empty((G, T) if scales_col_major else (T, G), dtype=torch.float32, device=dev)
-    if q.dtype not in (torch.uint8, torch.float8_e4m3fn) or q.numel() != T * H or not q.is_contiguous():
-        raise ValueError("q: expected contiguous uint8 / float8_e4m3fn [T, H]")
-    if scales.dtype != torch.float32 or scales.numel() != T * G or not scales.is_contiguous():
-        raise ValueError("scales: expected contiguous float32 [T, H/group_size]")
-    st = _lib.farn_reduce_add_rmsnorm_quant_group_ex(
-        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
-        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream),
-        variant | (SCALES_COL_MAJOR if scales_col_major else 0))
+    _check_buf("q", q, (torch.uint8, torch.float8_e4m3fn), T * H, dev)
+    _check_buf("scales", scales, (torch.float32,), T * G, dev)
+    st = _run(dev, _lib.farn_reduce_add_rmsnorm_quant_group_ex,
+              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
+              _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream),
+              variant | (SCALES_COL_MAJOR if scales_col_major else 0))
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
     return residual_out, out, q, scales
@@ -172,12 +196,13 @@ def reduce(partials, *, out=None, stream=None):
     sum of the partials. Returns out."""
     p0 = partials[0]
     T, H = p0.shape
-    dev = p0.device
+    dev = _device_of(p0)
     for i, p in enumerate(partials):
         _check_bf16(f"partials[{i}]", p, (T, H), dev)
     out = torch.empty_like(p0) if out is None else out
     _check_bf16("out", out, (T, H), dev)
-    st = _lib.farn_reduce(_ptr_array(partials), len(partials), T, H, _ptr(out), _stream(dev, stream))
+    st = _run(dev, _lib.farn_reduce, _ptr_array(partials), len(partials), T, H, _ptr(out),
+              _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce")
     return out
@@ -186,12 +211,15 @@ def reduce(partials, *, out=None, stream=None):
 def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None):
     """Per-group E4M3 quant alone of a bf16 [T,H] tensor. Returns (q uint8 [T,H], scales fp32 [T,H/128])."""
     T, H = x.shape
-    dev = x.device
+    dev = _device_of(x, "x")
     _check_bf16("x", x, (T, H), dev)
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
     G = H // group_size if group_size > 0 else 0
     scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
-    st = _lib.farn_quant_group(_ptr(x), T, H, group_size, _ptr(q), _ptr(scales), _stream(dev, stream))
+    _check_buf("q", q, (torch.uint8, torch.float8_e4m3fn), T * H, dev)
+    _check_buf("scales", scales, (torch.float32,), T * G, dev)
+    st = _run(dev, _lib.farn_quant_group, _ptr(x), T, H, group_size, _ptr(q), _ptr(scales),
+              _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_quant_group")
     return q, scales
@@ -205,26 +233,27 @@ def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, *, em
     scales uint8 [T, H/32])."""
     p0 = partials[0]
     T, H = p0.shape
-    dev = p0.device
+    dev = _device_of(p0)
     for i, p in enumerate(partials):
         _check_bf16(f"partials[{i}]", p, (T, H), dev)
     if residual is not None:
         _check_bf16("residual", residual, (T, H), dev)
     _check_bf16("gamma", gamma, (H,), dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    _check_bf16("residual_out", residual_out, (T, H), dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
+    if out is not None:
+        _check_bf16("out", out, (T, H), dev)
     q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev) if q is None else q
     scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None else scales
-    if q.dtype != torch.uint8 or q.numel() != T * (H // 2) or not q.is_contiguous():
-        raise ValueError("q: expected contiguous uint8 [T, H/2]")
-    if scales.dtype != torch.uint8 or scales.numel() != T * (H // MX_BLOCK) or not scales.is_contiguous():
-        raise ValueError("scales: expected contiguous uint8 [T, H/32]")
-    st = _lib.farn_reduce_add_rmsnorm_mxfp4_ex(
-        _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
-        _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
+    _check_buf("q", q, (torch.uint8,), T * (H // 2), dev)
+    _check_buf("scales", scales, (torch.uint8,), T * (H // MX_BLOCK), dev)
+    st = _run(dev, _lib.farn_reduce_add_rmsnorm_mxfp4_ex,
+              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
+              _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_mxfp4")
     return residual_out, out, q, scales
