@@ -1,6 +1,7 @@
 """Bench of the fused reduce + residual-add + RMSNorm (+ FP8 group-128 quant) op on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant V]
+                    [--cpu-budget S] [--no-secondary] [--sweep]
 
 A step is one call of the FP8 entry point (reduce, residual add, bf16 round,
 RMSNorm, per-group E4M3 quant, size-based dispatch) over one batch already resident
