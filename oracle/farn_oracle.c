@@ -228,13 +228,20 @@ static int run(job_t *proto) {
         jobs[k].nthreads = n;
         jobs[k].tid = k;
     }
-    for (int k = 1; k < n; ++k)
-        if (pthread_create(&th[k], NULL, worker, &jobs[k]) != 0) return -2;
-    if (worker(&jobs[0]) != NULL) rc = -3;
+    /* threads that did start are always joined before returning: they use `jobs` */
+    int started = 1;
     for (int k = 1; k < n; ++k) {
+        if (pthread_create(&th[k], NULL, worker, &jobs[k]) != 0) {
+            rc = -2;
+            break;
+        }
+        ++started;
+    }
+    if (rc == 0 && worker(&jobs[0]) != NULL) rc = -3;
+    for (int k = 1; k < started; ++k) {
         void *ret = NULL;
         pthread_join(th[k], &ret);
-        if (ret != NULL) rc = -3;
+        if (ret != NULL && rc == 0) rc = -3;
     }
     return rc;
 }

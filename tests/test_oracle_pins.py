@@ -607,6 +607,29 @@ MUTANTS = [
     ("mx_truncates", "double r = nearbyint(a / quantum) * quantum; /* ties to even multiple of the quantum */",
      "double r = floor(a / quantum) * quantum;"),
     ("mx_block_16", "const uint16_t *v = x + t * H + b * 32;", "const uint16_t *v = x + t * H + b * 16;"),
+    # rounding ties away from zero instead of to even
+    ("bf16_ties_away", "double r = nearbyint(a / quantum) * quantum;\n    if (r >= 0x1p128)",
+     "double r = round(a / quantum) * quantum;\n    if (r >= 0x1p128)"),
+    ("e4m3_ties_away", "double r = nearbyint(a / quantum) * quantum; /* in [0, 448] */",
+     "double r = round(a / quantum) * quantum;"),
+    ("mx_ties_away", "double r = nearbyint(a / quantum) * quantum; /* ties to even multiple of the quantum */",
+     "double r = round(a / quantum) * quantum;"),
+    # normalising the fp32 sum instead of the bf16 residual_out (both statistics and product)
+    ("norm_on_fp32_sum",
+     "/* One token row: steps 1-6 of the header, in order.",
+     "static double fp32_sum(const job_t *j, int64_t i) {\n"
+     "    float acc = bf16_to_float(j->partials[0][i]);\n"
+     "    for (int r = 1; r < j->R; ++r) acc = acc + bf16_to_float(j->partials[r][i]);\n"
+     "    if (j->residual) acc = acc + bf16_to_float(j->residual[i]);\n"
+     "    return (double)acc;\n}\n/* One token row: steps 1-6 of the header, in order.",
+     "double y = bf16_to_double(j->residual_out[base + h]);", "double y = fp32_sum(j, base + h);",
+     "double y = bf16_to_double(j->residual_out[base + h]);", "double y = fp32_sum(j, base + h);"),
+    ("group_amax_one_short", "for (int64_t h = h0; h < h0 + j->group; ++h) {\n                double v = fabs",
+     "for (int64_t h = h0; h < h0 + j->group - 1; ++h) {\n                double v = fabs"),
+    ("zero_group_unguarded", "if (scale == 0.0f)\n                    j->q[base + h] = 0x00u;\n                else\n",
+     "if (0)\n                    j->q[base + h] = 0x00u;\n                else\n"),
+    ("mx_zero_block_unguarded", "} else if (amax == 0.0) {", "} else if (amax < 0.0) {"),
+    ("mx_nan_block_unguarded", "if (isnan(a)) has_nan = 1;", "if (isnan(a)) has_nan = 0;"),
 ]
 
 
