@@ -72,6 +72,17 @@ def test_status_strings_and_select():
     assert F.select_variant(2, 8192, 4096, True) == F.VARIANT_BANDWIDTH  # two ranks
     assert F.select_variant(4, 8192, 4096, True) == F.VARIANT_LATENCY
     assert F.select_variant(2, 64, 4096, False) == F.VARIANT_LATENCY
+    # few ranks: the bandwidth shape's two vectors per lane keep more loads in flight
+    assert F.select_variant(2, 512, 3072, True) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(2, 256, 3072, False) == F.VARIANT_LATENCY
+    assert F.select_variant(2, 8192, 2560, False) == F.VARIANT_LATENCY  # nvec = 320
+    assert F.select_variant(2, 4096, 6144, True) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(2, 2048, 6144, True) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 2048, 3072, False) == F.VARIANT_BANDWIDTH  # plain only
+    assert F.select_variant(4, 2048, 3072, True) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 1024, 3072, False) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 4096, 6144, False) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 2048, 3072, False) == F.VARIANT_LATENCY
 
 
 class FakeCall:

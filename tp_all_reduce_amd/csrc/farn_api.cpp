@@ -108,7 +108,7 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
     return FARN_OK;
 }
 
-// AUTO rule, set from a measured sweep on MI355X: R = 8, 4 and 2; H = 2048 .. 8192;
+// AUTO rule, set from measured sweeps on MI355X: R = 8, 4 and 2; H = 1536 .. 8192;
 // T = 1 .. 8192; plain and FP8; graph replay, cache-hot; each point the median of 3 runs
 // with both shapes timed back to back (the shader clock drifts by up to 15 % between runs,
 // which had misled a single-pass sweep). By vectors per row (nvec = H/8; the latency shape
@@ -116,18 +116,27 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //   - nvec in (768, 1024] (H = 7168, 8192): bandwidth at every T and R: 1-10 % at decode
 //     sizes, up to 12 % at T = 1024..4096, 5-10 % for the FP8 prefill chunk (R = 8: 212
 //     against 223 us); at R = 8, H = 8192, T >= 1024 the two are within 1-2 %.
-//   - nvec in (256, 768] (H = 3072 .. 6144): latency (3-18 % at decode sizes), except
-//     H = 5120 at 1024 <= T < 2048, where bandwidth wins by 11 % (R = 8) and 6-10 % (R = 4),
-//     and two ranks at H = 4096 .. 5120 from T = 1024 (bandwidth by 2-7 %).
+//   - nvec in (256, 768] (H = 2056 .. 6144): latency (3-18 % at decode sizes), except
+//     H = 5120 at 1024 <= T < 2048, where bandwidth wins by 11 % (R = 8) and 6-10 % (R = 4).
+//   - Few ranks leave the latency shape only R + 1 loads in flight per lane; the bandwidth
+//     shape's two vectors per lane double that. Two ranks: bandwidth for H = 2568 .. 4096
+//     from T = 512 (up to 11 %, plain and FP8), H = 4096 .. 5120 from T = 1024 (2-7 %) and
+//     H = 5128 .. 6144 from T = 4096 (2-3 %). Four ranks, plain call: bandwidth for
+//     H = 2056 .. 4096 from T = 2048 (5-9 % at T = 2048; the FP8 call stays on latency,
+//     where its shorter per-lane code wins by up to 5 %).
 //   - nvec <= 256 (H <= 2048): latency up to T = 4096 (10-30 % at T <= 1024), bandwidth
 //     by 1-2 % at T = 8192.
 int select(int R, int64_t T, int64_t H, int quant) {
-    (void)quant;
     const int64_t nvec = H / 8;
     if (nvec <= 128) return FARN_VARIANT_LATENCY;  // one wave per row: no narrower shape
     if (nvec > 768 && nvec <= 1024) return FARN_VARIANT_BANDWIDTH;
     if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_BANDWIDTH;
-    if (R <= 2 && nvec > 448 && nvec <= 640 && T >= 1024) return FARN_VARIANT_BANDWIDTH;
+    if (R <= 2) {
+        if (nvec > 320 && nvec <= 512 && T >= 512) return FARN_VARIANT_BANDWIDTH;
+        if (nvec > 448 && nvec <= 640 && T >= 1024) return FARN_VARIANT_BANDWIDTH;
+        if (nvec > 640 && nvec <= 768 && T >= 4096) return FARN_VARIANT_BANDWIDTH;
+    }
+    if (R > 2 && R <= 4 && !quant && nvec > 256 && nvec <= 512 && T >= 2048) return FARN_VARIANT_BANDWIDTH;
     if (nvec <= 256 && T >= 8192) return FARN_VARIANT_BANDWIDTH;
     return FARN_VARIANT_LATENCY;
 }
