@@ -119,7 +119,8 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //   - nvec in (256, 768] (H = 2056 .. 6144): latency (3-18 % at decode sizes), except
 //     H = 5120 at 1024 <= T < 2048, where bandwidth wins by 11 % (R = 8) and 6-10 % (R = 4).
 //   - Few ranks leave the latency shape only R + 1 loads in flight per lane; the bandwidth
-//     shape's two vectors per lane double that. Two ranks: bandwidth for H = 2568 .. 4096
+//     shape's two vectors per lane double that, and since both shapes then reach the limit of
+//     8 waves per SIMD, the loads in flight per compute unit double too. Two ranks: bandwidth for H = 2568 .. 4096
 //     from T = 512 (up to 11 %, plain and FP8), H = 4096 .. 5120 from T = 1024 (2-7 %) and
 //     H = 5128 .. 6144 from T = 4096 (2-3 %). Four ranks, plain call: bandwidth for
 //     H = 2056 .. 4096 from T = 2048 (5-9 % at T = 2048; the FP8 call stays on latency,
