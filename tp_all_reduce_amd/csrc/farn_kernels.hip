@@ -263,13 +263,13 @@ __device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
     return packed;
 }
 
-// fold_slot, stored as residual_out, with the squares of the rounded values added to ss
-// (fp64; zeros from lanes past the row end add nothing).
-template <int R>
+// fold_slot, stored as residual_out here (kStoreNow) or by the caller later, with the squares
+// of the rounded values added to ss (fp64; zeros from lanes past the row end add nothing).
+template <int R, bool kStoreNow>
 __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
                                              uint32_t off, double &ss) {
     const u32x4 packed = fold_slot<R>(in, k.res != nullptr);
-    st16(packed, ro_out, off);
+    if constexpr (kStoreNow) st16(packed, ro_out, off);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const double a = (double)bf_lo(packed[w]);
@@ -405,20 +405,25 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const int rb = k.nvec * 16;
     const int64_t ro = t * (int64_t)rb;
     const rsrc_t r_ro = row_rsrc(k.res_out, ro, rb);
+    // The plain two-slot kernel stores residual_out with out, after the statistics, rather
+    // than between the two slots' folds while slot 1's loads are in flight: measured 5-8 %
+    // faster at decode sizes (H = 7168, 8192) and ~1 % on the prefill chunk. The quant and
+    // one-slot kernels measured slower that way (1-3 %) and store it as soon as it is folded.
+    constexpr bool kDefer = QM == kQuantNone && VPL == 2;
     double ss = 0.0;
     u32x4 yb[VPL];
     if constexpr (VPL == 2) {
         SlotIn<R> in1;
         load_slot<R>(in1, k, t, off0 + L16);
-        yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
-        yb[1] = reduce_slot<R>(in1, k, r_ro, off0 + L16, ss);
+        yb[0] = reduce_slot<R, !kDefer>(in0, k, r_ro, off0, ss);
+        yb[1] = reduce_slot<R, !kDefer>(in1, k, r_ro, off0 + L16, ss);
     } else {
-        yb[0] = reduce_slot<R>(in0, k, r_ro, off0, ss);
+        yb[0] = reduce_slot<R, true>(in0, k, r_ro, off0, ss);
 #pragma unroll
         for (int v = 1; v < VPL; ++v) {
             SlotIn<R> in;
             load_slot<R>(in, k, t, off0 + v * L16);
-            yb[v] = reduce_slot<R>(in, k, r_ro, off0 + v * L16, ss);
+            yb[v] = reduce_slot<R, true>(in, k, r_ro, off0 + v * L16, ss);
         }
     }
     const double rstd = row_rstd(ss, k, slot);
@@ -435,8 +440,10 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const uint32_t sbase = cols ? (uint32_t)t * 4u : 0u;
     const uint32_t sstride = cols ? (uint32_t)k.T * 4u : 4u;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
+    for (int v = 0; v < VPL; ++v) {
+        if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
         store_slot<QM>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16, sbase, sstride);
+    }
 }
 
 template <int VPL>
