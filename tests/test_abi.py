@@ -83,6 +83,12 @@ def test_status_strings_and_select():
     assert F.select_variant(4, 1024, 3072, False) == F.VARIANT_LATENCY
     assert F.select_variant(4, 4096, 6144, False) == F.VARIANT_LATENCY
     assert F.select_variant(8, 2048, 3072, False) == F.VARIANT_LATENCY
+    # plain call above H = 7168 from T = 2048: latency shape
+    assert F.select_variant(8, 8192, 8192, False) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 2048, 8192, False) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 1024, 8192, False) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(8, 8192, 8192, True) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(8, 8192, 7168, False) == F.VARIANT_BANDWIDTH
 
 
 class FakeCall:

@@ -115,7 +115,9 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 // runs one vector per lane, the bandwidth shape half as many lanes with two vectors each):
 //   - nvec in (768, 1024] (H = 7168, 8192): bandwidth at every T and R: 1-10 % at decode
 //     sizes, up to 12 % at T = 1024..4096, 5-10 % for the FP8 prefill chunk (R = 8: 212
-//     against 223 us); at R = 8, H = 8192, T >= 1024 the two are within 1-2 %.
+//     against 223 us); except the plain call above H = 7168 from T = 2048, where the
+//     latency shape wins by 2-4 % (the bandwidth shape's late residual_out store, a gain
+//     at decode sizes, costs a little there).
 //   - nvec in (256, 768] (H = 2056 .. 6144): latency (3-18 % at decode sizes), except
 //     H = 5120 at 1024 <= T < 2048, where bandwidth wins by 11 % (R = 8) and 6-10 % (R = 4).
 //   - Few ranks leave the latency shape only R + 1 loads in flight per lane; the bandwidth
@@ -130,7 +132,8 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 int select(int R, int64_t T, int64_t H, int quant) {
     const int64_t nvec = H / 8;
     if (nvec <= 128) return FARN_VARIANT_LATENCY;  // one wave per row: no narrower shape
-    if (nvec > 768 && nvec <= 1024) return FARN_VARIANT_BANDWIDTH;
+    if (nvec > 768 && nvec <= 1024)
+        return (!quant && nvec > 896 && T >= 2048) ? FARN_VARIANT_LATENCY : FARN_VARIANT_BANDWIDTH;
     if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_BANDWIDTH;
     if (R <= 2) {
         if (nvec > 320 && nvec <= 512 && T >= 512) return FARN_VARIANT_BANDWIDTH;
