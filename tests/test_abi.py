@@ -80,9 +80,16 @@ def test_status_strings_and_select():
     assert F.select_variant(2, 2048, 6144, True) == F.VARIANT_LATENCY
     assert F.select_variant(4, 2048, 3072, False) == F.VARIANT_BANDWIDTH  # plain only
     assert F.select_variant(4, 2048, 3072, True) == F.VARIANT_LATENCY
-    assert F.select_variant(4, 1024, 3072, False) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 1024, 3072, False) == F.VARIANT_BANDWIDTH  # mid-T band
     assert F.select_variant(4, 4096, 6144, False) == F.VARIANT_LATENCY
     assert F.select_variant(8, 2048, 3072, False) == F.VARIANT_LATENCY
+    # up to four ranks, plain, mid T: bandwidth shape
+    assert F.select_variant(4, 512, 6144, False) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(2, 512, 6144, False) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(4, 512, 6144, True) == F.VARIANT_LATENCY
+    assert F.select_variant(8, 512, 6144, False) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 256, 6144, False) == F.VARIANT_LATENCY
+    assert F.select_variant(4, 2048, 6144, False) == F.VARIANT_LATENCY
     # plain call above H = 7168 from T = 2048: latency shape
     assert F.select_variant(8, 8192, 8192, False) == F.VARIANT_LATENCY
     assert F.select_variant(8, 2048, 8192, False) == F.VARIANT_LATENCY

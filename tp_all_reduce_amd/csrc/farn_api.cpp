@@ -126,7 +126,9 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //     from T = 512 (up to 11 %, plain and FP8), H = 4096 .. 5120 from T = 1024 (2-7 %) and
 //     H = 5128 .. 6144 from T = 4096 (2-3 %). Four ranks, plain call: bandwidth for
 //     H = 2056 .. 4096 from T = 2048 (5-9 % at T = 2048; the FP8 call stays on latency,
-//     where its shorter per-lane code wins by up to 5 %).
+//     where its shorter per-lane code wins by up to 5 %). Up to four ranks, plain call,
+//     H = 2056 .. 6144 at 512 <= T < 2048: bandwidth (2-9 % at T = 512, measured after the
+//     plain two-slot kernel moved its residual_out store after the statistics).
 //   - nvec <= 256 (H <= 2048): latency up to T = 4096 (10-30 % at T <= 1024), bandwidth
 //     by 1-2 % at T = 8192.
 int select(int R, int64_t T, int64_t H, int quant) {
@@ -141,6 +143,7 @@ int select(int R, int64_t T, int64_t H, int quant) {
         if (nvec > 640 && nvec <= 768 && T >= 4096) return FARN_VARIANT_BANDWIDTH;
     }
     if (R > 2 && R <= 4 && !quant && nvec > 256 && nvec <= 512 && T >= 2048) return FARN_VARIANT_BANDWIDTH;
+    if (R <= 4 && !quant && nvec > 256 && nvec <= 768 && T >= 512 && T < 2048) return FARN_VARIANT_BANDWIDTH;
     if (nvec <= 256 && T >= 8192) return FARN_VARIANT_BANDWIDTH;
     return FARN_VARIANT_LATENCY;
 }
