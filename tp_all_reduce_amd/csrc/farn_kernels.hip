@@ -93,6 +93,9 @@ constexpr int kLoadPolicy = 2;
 constexpr int kGammaLoadPolicy = 0;
 constexpr int kStoreBf16Policy = 16;
 constexpr int kStoreCodePolicy = 2;
+// MXFP4 codes and scale bytes: sc1 (measured: -0.4 % on the prefill chunk, -3.5 % at decode
+// against non-temporal; for the FP8 codes non-temporal is the faster one by 3.5-7 %).
+constexpr int kStoreMxPolicy = 16;
 constexpr uint32_t kDropOffset = 0x80000000u;  // beyond any row: store dropped
 
 __device__ __forceinline__ rsrc_t row_rsrc(const void *base, int64_t byte_off, int nbytes) {
@@ -111,11 +114,11 @@ __device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void st4(float v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kStoreCodePolicy);
 }
-__device__ __forceinline__ void st4u(uint32_t v, rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStoreCodePolicy);
+__device__ __forceinline__ void st4_mx(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStoreMxPolicy);
 }
-__device__ __forceinline__ void st1(uint32_t v, rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, kStoreCodePolicy);
+__device__ __forceinline__ void st1_mx(uint32_t v, rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, kStoreMxPolicy);
 }
 
 // ---------------------------------------------------------------- number formats
@@ -370,10 +373,10 @@ __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[4], o[5], sc, 2);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[6], o[7], sc, 3);
     const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
-    st4u(word & keep, r_q, off >> 2);
+    st4_mx(word & keep, r_q, off >> 2);
     const uint32_t sbyte = nan_blk ? 0xffu : (zero_blk ? 0u : (uint32_t)(sexp + 127));
     // one lane per quad writes the scale byte; the others aim past the row (dropped)
-    st1(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
+    st1_mx(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
 }
 
 // Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16), store
