@@ -198,6 +198,30 @@ def test_in_place_residual(dev):
         assert ok, why
 
 
+def test_in_place_residual_quant(dev):
+    """In place with the FP8 and MXFP4 calls too (their kernels store residual_out at a
+    different point of the row than the plain two-slot kernel)."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=11, T=21)
+    ref = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
+    ref_mx = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
+    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+        say(f"[gpu] in-place residual, FP8 and MXFP4, variant={variant}")
+        u = Uploaded(d, dev)
+        ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, residual_out=u.res, variant=variant)
+        torch.cuda.synchronize()
+        assert ro.data_ptr() == u.res.data_ptr() and np.array_equal(from_dev_bf16(ro), ref[0])
+        ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro), ref[0]),
+                                   compare_bf16("out", from_dev_bf16(out), ref[1]),
+                                   compare_fp8(q.cpu().numpy(), ref[2], sc.cpu().numpy(), ref[3]))
+        assert ok, why
+        u = Uploaded(d, dev)
+        ro, out, q, sc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, residual_out=u.res, variant=variant)
+        torch.cuda.synchronize()
+        assert ro.data_ptr() == u.res.data_ptr() and np.array_equal(from_dev_bf16(ro), ref_mx[0])
+        ok, why = mxfp4_within_tolerance(compare_mxfp4(q.cpu().numpy(), ref_mx[2], sc.cpu().numpy(), ref_mx[3]))
+        assert ok, why
+
+
 def test_empty_T(dev):
     say("[gpu] T = 0")
     p = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
