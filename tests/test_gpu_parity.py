@@ -565,6 +565,38 @@ def test_plain_c_client():
     assert "0 mismatches" in proc.stdout
 
 
+# ------------------------------------------------------------------ row schedules
+@pytest.mark.parametrize("quant", ["fp8", "mxfp4"])
+def test_small_and_streaming_schedules_agree(dev, quant):
+    """The two-slot quant kernels store in a different order for few rows (T <= 512) than for
+    many; results must not depend on it. The same 512 rows run as a 512-row call (small-call
+    schedule) and inside a 520-row call (streaming schedule), bandwidth shape, and every output
+    byte of those rows must agree; the small call is also checked against the oracle."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=77, T=520)
+    u = Uploaded(d, dev)
+    P512 = [p[:512] for p in u.P]
+    call = F.reduce_add_rmsnorm_quant_group if quant == "fp8" else F.reduce_add_rmsnorm_mxfp4
+    say(f"[gpu] schedules agree ({quant}): T=512 vs T=520")
+    big = call(u.P, u.res, u.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    small = call(P512, u.res[:512], u.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    torch.cuda.synchronize()
+    for a, b in zip(small, big):
+        assert torch.equal(a.view(torch.uint8), b[:512].contiguous().view(torch.uint8))
+    if quant == "fp8":
+        r = oracle.reduce_add_rmsnorm_quant_group(d["partials"][:, :512], d["residual"][:512], d["gamma"], EPS,
+                                                  nthreads=8)
+        ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(small[0]), r[0]),
+                                   compare_bf16("out", from_dev_bf16(small[1]), r[1]),
+                                   compare_fp8(small[2].cpu().numpy(), r[2], small[3].cpu().numpy(), r[3]))
+    else:
+        r = oracle.reduce_add_rmsnorm_mxfp4(d["partials"][:, :512], d["residual"][:512], d["gamma"], EPS, nthreads=8)
+        ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(small[0]), r[0]),
+                                   compare_bf16("out", from_dev_bf16(small[1]), r[1]), None)
+        ok2, why2 = mxfp4_within_tolerance(compare_mxfp4(small[2].cpu().numpy(), r[2], small[3].cpu().numpy(), r[3]))
+        ok, why = ok and ok2, f"{why} {why2}"
+    assert ok, why
+
+
 # ------------------------------------------------------------------ binding checks
 def test_binding_rejects_bad_output_buffers(dev):
     """Output buffers of the wrong shape, dtype or device are refused by the binding before

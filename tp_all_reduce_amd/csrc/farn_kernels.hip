@@ -93,6 +93,8 @@ constexpr int kLoadPolicy = 2;
 constexpr int kGammaLoadPolicy = 0;
 constexpr int kStoreBf16Policy = 16;
 constexpr int kStoreCodePolicy = 2;
+// FP8 codes and scales of the two-slot kernel's small-call schedule (few rows): sc1.
+constexpr int kStoreCodeSmallPolicy = 16;
 // MXFP4 codes and scale bytes: sc1 (measured: -0.4 % on the prefill chunk, -3.5 % at decode
 // against non-temporal; for the FP8 codes non-temporal is the faster one by 3.5-7 %).
 constexpr int kStoreMxPolicy = 16;
@@ -108,11 +110,13 @@ __device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void st16(u32x4 v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreBf16Policy);
 }
+template <int P>
 __device__ __forceinline__ void st8(u32x2 v, rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreCodePolicy);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, P);
 }
+template <int P>
 __device__ __forceinline__ void st4(float v, rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kStoreCodePolicy);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, P);
 }
 __device__ __forceinline__ void st4_mx(uint32_t v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStoreMxPolicy);
@@ -318,6 +322,7 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
 // A group whose scale is below 2^-64 is quantised from o and scale both times 2^64 (exact;
 // the quotient is the same), so that 1/scale and the remainder stay normal numbers; the
 // stored scale is the unscaled one.
+template <int P>
 __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
                                            uint32_t sstride) {
     u16x2 m = u16x2{0, 0};
@@ -345,10 +350,10 @@ __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, ui
         word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2], v[4 * d + 3], word, true);
         codes[d] = (uint32_t)word & keep;
     }
-    st8(codes, r_q, off >> 1);
+    st8<P>(codes, r_q, off >> 1);
     // one lane per group writes the scale; the others aim past the row (dropped)
     const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off >> 8) * sstride : kDropOffset;
-    st4(scale, r_sc, soff);
+    st4<P>(scale, r_sc, soff);
 }
 
 // MXFP4 of one vector slot: the 32-channel block spans the 4 lanes of a quad. Shared
@@ -379,13 +384,23 @@ __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc
     st1_mx(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
 }
 
-// Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16), store
-// out, and (QM) its quantised codes and scales.
-template <int QM>
-__device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out,
-                                           rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
-                                           uint32_t sstride) {
-    float o[8];
+// Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16) and store it
+// as out; returns the packed bf16 values (the FP8 quant's input).
+__device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out, uint32_t off) {
+    u32x4 packed;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const double lo = ((double)bf_lo(yb[w]) * rstd) * (double)bf_lo(gam[w]);
+        const double hi = ((double)bf_hi(yb[w]) * rstd) * (double)bf_hi(gam[w]);
+        packed[w] = pack_bf16_d(lo, hi);
+    }
+    st16(packed, r_out, off);
+    return packed;
+}
+
+// norm_store that also returns the values as floats in `o` (the MXFP4 quant's input).
+__device__ __forceinline__ void norm_store_f(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out, uint32_t off,
+                                             float (&o)[8]) {
     u32x4 packed;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -396,15 +411,13 @@ __device__ __forceinline__ void store_slot(u32x4 yb, u32x4 gam, double rstd, rsr
         o[2 * w + 1] = bf_hi(packed[w]);
     }
     st16(packed, r_out, off);
-    if constexpr (QM == kQuantFp8) quant_slot(packed, r_q, r_sc, off, sbase, sstride);
-    if constexpr (QM == kQuantMxfp4) mxfp4_slot(o, r_q, r_sc, off);
 }
 
 // Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
 // lane the source issues the second slot's loads before reducing the first; with four
 // (rows beyond 16384 channels) the slots are loaded and reduced one after the other, to
 // bound register use.
-template <int R, int VPL, int QM>
+template <int R, int VPL, int QM, bool kSmall>
 __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
                                        const Params &k, int64_t t, double *slot) {
     const uint32_t L16 = blockDim.x * 16u;
@@ -412,11 +425,18 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const int rb = k.nvec * 16;
     const int64_t ro = t * (int64_t)rb;
     const rsrc_t r_ro = row_rsrc(k.res_out, ro, rb);
-    // The plain two-slot kernel stores residual_out with out, after the statistics, rather
-    // than between the two slots' folds while slot 1's loads are in flight: measured 5-8 %
-    // faster at decode sizes (H = 7168, 8192) and ~1 % on the prefill chunk. The quant and
-    // one-slot kernels measured slower that way (1-3 %) and store it as soon as it is folded.
-    constexpr bool kDefer = QM == kQuantNone && VPL == 2;
+    // Store schedule, chosen by measurement on MI355X. The plain two-slot kernel stores
+    // residual_out with out, after the statistics, rather than between the two slots' folds
+    // while slot 1's loads are in flight: 5-8 % faster at decode sizes (H = 7168, 8192) and
+    // ~1 % on the prefill chunk. The one-slot kernels store it as soon as it is folded (1-3 %
+    // faster that way). The two-slot quant kernels have two schedules: the streaming one
+    // (immediate residual_out, each slot's codes right after its out, FP8 codes
+    // non-temporal) for many rows, and kSmall (residual_out after the statistics, FP8: all of
+    // out before the codes, codes and scales sc1) for few rows, where it is 4-15 % faster
+    // (T = 16 .. 256) and from T = 1024 2-6 % slower.
+    constexpr bool kDefer = VPL == 2 && (QM == kQuantNone || kSmall);
+    constexpr bool kOutsFirst = kSmall && QM == kQuantFp8 && VPL == 2;
+    constexpr int kCodeP = kSmall ? kStoreCodeSmallPolicy : kStoreCodePolicy;
     double ss = 0.0;
     u32x4 yb[VPL];
     if constexpr (VPL == 2) {
@@ -446,10 +466,28 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
                              : row_rsrc(k.scales, t * (int64_t)sb, sb);
     const uint32_t sbase = cols ? (uint32_t)t * 4u : 0u;
     const uint32_t sstride = cols ? (uint32_t)k.T * 4u : 4u;
+    if constexpr (kOutsFirst) {
+        u32x4 ob[VPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-        if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
-        store_slot<QM>(yb[v], gam[v], rstd, r_out, r_q, r_sc, off0 + v * L16, sbase, sstride);
+        for (int v = 0; v < VPL; ++v) {
+            st16(yb[v], r_ro, off0 + v * L16);
+            ob[v] = norm_store(yb[v], gam[v], rstd, r_out, off0 + v * L16);
+        }
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) quant_slot<kCodeP>(ob[v], r_q, r_sc, off0 + v * L16, sbase, sstride);
+    } else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
+            if constexpr (QM == kQuantMxfp4) {
+                float o[8];
+                norm_store_f(yb[v], gam[v], rstd, r_out, off0 + v * L16, o);
+                mxfp4_slot(o, r_q, r_sc, off0 + v * L16);
+            } else {
+                const u32x4 ob = norm_store(yb[v], gam[v], rstd, r_out, off0 + v * L16);
+                if constexpr (QM == kQuantFp8) quant_slot<kCodeP>(ob, r_q, r_sc, off0 + v * L16, sbase, sstride);
+            }
+        }
     }
 }
 
@@ -463,7 +501,7 @@ __device__ __forceinline__ void load_gamma(u32x4 (&gam)[VPL], const Params &k) {
 }
 
 // ---------------------------------------------------------------- kernels
-template <int R, int VPL, int QM>
+template <int R, int VPL, int QM, bool kSmall>
 __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     __shared__ double slot[kMaxWaves];
     const int64_t t = k.t0 + blockIdx.x;
@@ -471,7 +509,7 @@ __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     load_slot<R>(in, k, t, threadIdx.x * 16u);
     u32x4 gam[VPL];
     load_gamma<VPL>(gam, k);
-    do_row<R, VPL, QM>(in, gam, k, t, slot);
+    do_row<R, VPL, QM, kSmall>(in, gam, k, t, slot);
 }
 
 // Unfused building blocks (the compositions the fused call replaces): the all-reduce
@@ -503,15 +541,18 @@ __global__ __launch_bounds__(1024) void farn_quant_rows(const Params k) {
     for (int v = 0; v < VPL; ++v) xv[v] = ld16(r_x, (v * blockDim.x + threadIdx.x) * 16u);
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-        quant_slot(xv[v], r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
+        quant_slot<kStoreCodePolicy>(xv[v], r_q, r_sc, (v * blockDim.x + threadIdx.x) * 16u, 0u, 4u);
 }
 
 // ---------------------------------------------------------------- dispatch tables
 typedef void (*KernelFn)(const Params);
 
+// Entries: one, two and four vector slots per lane, then the two-slot small-call schedule
+// (the plain kernel has one schedule: its entry 3 is entry 1).
 template <int R, int QM>
 struct Row {
-    static constexpr KernelFn fn[3] = {farn_rows<R, 1, QM>, farn_rows<R, 2, QM>, farn_rows<R, 4, QM>};
+    static constexpr KernelFn fn[4] = {farn_rows<R, 1, QM, false>, farn_rows<R, 2, QM, false>,
+                                       farn_rows<R, 4, QM, false>, farn_rows<R, 2, QM, QM != kQuantNone>};
 };
 
 template <int R>
@@ -568,9 +609,14 @@ static Params make_params(const Call &c) {
     return k;
 }
 
+// Rows up to which the two-slot quant kernels use their small-call schedule (measured on
+// MI355X: faster up to T = 256, slower from T = 1024).
+constexpr int64_t kSmallRows = 512;
+
 int launch(const Call &c, int variant) {
     const RowShape rs = row_shape(c.H, c.kind == Kind::kFused ? variant : 1);
-    const int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
+    int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
+    if (c.kind == Kind::kFused && c.q != nullptr && rs.vpl == 2 && c.T <= kSmallRows) vi = 3;
     KernelFn fn = nullptr;
     if (c.kind == Kind::kReduce) {
         fn = pick_reduce(c.R, vi);
