@@ -27,11 +27,13 @@
 //   latency   - the widest row mapping (L up to 1024, one vector per lane up to H =
 //               8192): the fewest instructions per lane.
 //   bandwidth - a narrow mapping (L about NV/2, two vectors per lane): half the waves
-//               per row, which fill a compute unit's four SIMDs differently. On MI355X it
-//               is the faster one for H = 7168 and 8192 at every T (the FP8 prefill call
-//               at H = 7168: 212 against 223 us), the slower one for H = 3072 .. 6144.
+//               per row, twice the loads in flight per lane. On MI355X it is the faster
+//               one for H = 7168 and 8192 (the FP8 prefill call at H = 7168: 212 against
+//               223 us) and, with two or four ranks, for mid-size and large T at
+//               H = 2048 .. 6144; at eight ranks the latency shape wins there.
 // The fp64 statistics make the two shapes agree bit for bit in practice (their sums
-// of squares differ only in the order of fp64 additions).
+// of squares differ only in the order of fp64 additions). The two-slot quant kernels
+// also have two store schedules, one for many rows and one for few (do_row).
 //
 // No MFMA: nothing here is a contraction; the op is HBM-bound (about 0.5 flop per
 // byte against a ridge of ~20 flop/byte).
