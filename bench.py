@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import tp_all_reduce_amd as F  # noqa: E402  (raises if the HIP library is not built)
-from gen import CONFIGS, SWEEP_T, make_inputs, sweep_config  # noqa: E402
+from gen import CONFIGS, SWEEP_T, Config, make_inputs, sweep_config  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
 METRIC = "effective HBM GB/s (% of MI355X peak) and µs/call of fused reduce+RMSNorm"
@@ -334,7 +334,34 @@ def secondary(dev, steps):
     cfg, quant, emit = WORKLOADS["decode_ds_mxfp4"]
     b = Bufs(make_inputs(cfg), dev, quant, emit)
     out["decode_ds_mxfp4"] = {"us_per_call_graph_hot": round(median_graph([b], F.VARIANT_AUTO, 200, 10) * 1e3, 2)}
+    out["launch_floor"] = launch_floor(dev)
     return out
+
+
+class _Fill:
+    """A one-element fill: torch's smallest kernel, as a bare-launch reference."""
+
+    def __init__(self, dev):
+        self.x = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def call(self, variant):
+        self.x.fill_(1.0)
+
+
+def launch_floor(dev):
+    """What a decode call costs before it moves any data, by graph replay (median of 3),
+    cache-hot: a bare launch (a one-element fill), the fused call on one row of one wave
+    (R = 1, T = 1, H = 512), and one row of the decode shape (R = 8, T = 1, H = 7168: the
+    dependent chain of loads, fold, row statistics and stores that every row of a decode
+    call runs, on one compute unit)."""
+    res = {"bare_launch_us": round(median_graph([_Fill(dev)], 0, 200, 10) * 1e3, 2)}
+    for label, (R, T, H) in (("fused_one_wave_us", (1, 1, 512)), ("fused_one_decode_row_us", (8, 1, 7168))):
+        cfg = Config(label, R=R, T=T, H=H, quant=(False,))
+        b = Bufs(make_inputs(cfg), dev, False, True)
+        res[label] = round(median_graph([b], F.VARIANT_AUTO, 200, 10) * 1e3, 2)
+        del b
+    res["what"] = "graph replay, cache-hot, median of 3; us per call"
+    return res
 
 
 def sweep(dev):
