@@ -367,13 +367,18 @@ def launch_floor(dev):
 def sweep(dev):
     """The message-size sweep (R = 8, H = 8192, T = 2 .. 4096, plain call) in us/call by graph
     replay: hot (one buffer set, cache-resident) and cold (sets rotated over >= 1 GiB, so every
-    call streams from HBM rather than the 256 MB last-level cache), with the cold rate."""
+    call streams from HBM rather than the 256 MB last-level cache), with the cold rate, and
+    both launch shapes forced (hot) beside the one the dispatch rule picks."""
     out = {}
     for T in SWEEP_T:
         cfg = sweep_config(T)
         b = Bufs(make_inputs(cfg), dev, False, True)
         nb = nbytes(cfg, False, True)
         hot = median_graph([b], F.VARIANT_AUTO, 200, 10)
+        # both launch shapes forced, timed right after (hot), as the dispatch rule was set; before
+        # the cold leg, whose rotation over 1 GiB leaves the caches in another state
+        forced = {name: round(median_graph([b], v, 200, 10) * 1e3, 2)
+                  for name, v in (("latency", F.VARIANT_LATENCY), ("bandwidth", F.VARIANT_BANDWIDTH))}
         k = max(1, -(-(1 << 30) // nb))
         sets = [b] + [b.clone(dev) for _ in range(k - 1)]
         calls = k * max(1, 200 // k)
@@ -382,7 +387,8 @@ def sweep(dev):
         out[f"T{T}"] = {"us_per_call_graph_hot": round(hot * 1e3, 2), "us_per_call_graph_cold": round(cold * 1e3, 2),
                         "GBps_graph_cold": round(gbps, 1), "pct_of_peak_cold": round(100 * gbps / PEAK_HBM_GBPS, 1),
                         "rotation_sets": k, "bytes_per_call": nb,
-                        "variant": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)]}
+                        "variant": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)],
+                        "forced_hot_us": forced}
         log(f"sweep T={T}: {out[f'T{T}']}")
         del sets, b
         torch.cuda.empty_cache()
