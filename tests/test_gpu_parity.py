@@ -129,6 +129,23 @@ def test_prefill_full_size_properties(prefill):
     assert ((a[2] & 0x7F) == 0x7E).view(prefill.T, -1, 128).any(dim=2).all()  # a 448 code per group
 
 
+@pytest.mark.parametrize("R,H", [(6, 7168), (8, 6656)])
+def test_two_workgroups_per_cu_launch(dev, R, H):
+    """The plain call's bandwidth shape at H = 6152..7168 with R >= 6 and T >= 2048 is launched
+    with LDS reserved so that at most two workgroups share a compute unit: its outputs match the
+    oracle on sampled rows, and the latency shape (launched without the reservation) bit for bit
+    on every row."""
+    T = 2048
+    u = Uploaded(make_inputs(CONFIGS["prefill"], seed=40 + R, R=R, T=T, H=H), dev)
+    assert F.select_variant(R, T, H, False) == F.VARIANT_BANDWIDTH
+    run_and_compare(u, False, "auto", rows=_sample_rows(T, 32, seed=R), label="two-per-CU")
+    a = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    b = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_LATENCY)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 @pytest.mark.parametrize("T", [2, 8, 64, 256, 1024, 4096])
 def test_sweep_points(dev, T):
     cfg = sweep_config(T)

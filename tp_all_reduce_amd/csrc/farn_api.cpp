@@ -148,6 +148,23 @@ int select(int R, int64_t T, int64_t H, int quant) {
     return FARN_VARIANT_LATENCY;
 }
 
+// Workgroups per compute unit for the plain call in the two-slot (bandwidth) shape at
+// H = 6152 .. 7168, where 76 VGPRs let three workgroups of 7 waves share a compute unit.
+// Two stream the prefill traffic faster: reserving 56 KiB of LDS per workgroup (of 160 KiB
+// per compute unit) leaves room for only two. Measured on MI355X (median of 5, interleaved,
+// eager back-to-back calls): R = 8, H = 7168: -2.9 % at T = 2048, -2.3 % at T = 4096, -1.9 %
+// at T = 8192 (205.4 -> 201.4 us); R = 8, H = 6656: -3.9 % at T = 2048; R = 7: -1.7 .. -2.0 %
+// and R = 6: -0.6 .. -1.3 % at T = 8192. No change at T <= 1024 (R = 8) and for the FP8 and
+// MXFP4 calls (register-bound to about two already); slower with fewer ranks (R = 5: +1 ..
+// +3 %, R = 4: +1.9 %, R = 2: +4.6 %) and no gain at H = 8192.
+constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
+
+unsigned lds_reserve(int R, int64_t T, int64_t H, Quant quant, int shape) {
+    const int64_t nvec = H / 8;
+    const bool two_slot = shape == FARN_VARIANT_BANDWIDTH && nvec > 768 && nvec <= 896;
+    return (quant == kNone && two_slot && R >= 6 && T >= 2048) ? kLdsTwoPerCu : 0u;
+}
+
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
                 float eps, int64_t T, int64_t H, int group_size, Quant quant, void *residual_out,
                 void *out, void *q, void *scales, void *stream, int options) {
@@ -178,6 +195,7 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     c.mxfp4 = quant == kMxfp4;
     c.scale_cols = cols;
     c.stream = stream;
+    c.lds_reserve = lds_reserve(R, T, H, quant, shape);
     return farn::launch(c, shape) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
@@ -229,6 +247,7 @@ farn::Call blank_call(void *stream) {
     c.scales = nullptr;
     c.x = nullptr;
     c.stream = stream;
+    c.lds_reserve = 0;
     return c;
 }
 

@@ -26,6 +26,9 @@ struct Call {
     bool scale_cols = false;  // FP8 scales column-major [H/128, T]
     const void *x = nullptr;  // kQuant input
     void *stream;
+    // Bytes of LDS reserved per workgroup beyond what the kernel declares (unused by it):
+    // bounds how many workgroups share a compute unit (0 = no bound).
+    unsigned lds_reserve = 0;
 };
 
 // Lanes per token row (= workgroup size) and 16-byte vectors per lane for hidden size

@@ -33,7 +33,10 @@
 //               H = 2048 .. 6144; at eight ranks the latency shape wins there.
 // The fp64 statistics make the two shapes agree bit for bit in practice (their sums
 // of squares differ only in the order of fp64 additions). The two-slot quant kernels
-// also have two store schedules, one for many rows and one for few (do_row).
+// also have two store schedules, one for many rows and one for few (do_row). The host
+// may reserve LDS that the kernel does not use (Call::lds_reserve) to bound how many
+// workgroups share a compute unit: the plain two-slot kernel at H = 6152 .. 7168 streams
+// large T faster with two per compute unit than with the three its registers allow.
 //
 // No MFMA: nothing here is a contraction; the op is HBM-bound (about 0.5 flop per
 // byte against a ridge of ~20 flop/byte).
@@ -640,8 +643,8 @@ int launch(const Call &c, int variant) {
     for (int64_t t0 = 0; t0 < c.T; t0 += max_rows) {
         k.t0 = t0;
         const int64_t n = c.T - t0 < max_rows ? c.T - t0 : max_rows;
-        if (hipLaunchKernel((const void *)fn, dim3((uint32_t)n), dim3((uint32_t)rs.lanes), args, 0,
-                            (hipStream_t)c.stream) != hipSuccess)
+        if (hipLaunchKernel((const void *)fn, dim3((uint32_t)n), dim3((uint32_t)rs.lanes), args,
+                            c.lds_reserve, (hipStream_t)c.stream) != hipSuccess)
             return 1;
     }
     return 0;
