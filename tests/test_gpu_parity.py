@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import tp_all_reduce_amd as F
-from gen import CONFIGS, make_inputs, sweep_config
+from gen import CONFIGS, SWEEP_T, make_inputs, sweep_config
 from parity import (compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16, mxfp4_within_tolerance,
                     to_dev_bf16, within_tolerance)
 
@@ -146,7 +146,7 @@ def test_two_workgroups_per_cu_launch(dev, R, H):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-@pytest.mark.parametrize("T", [2, 8, 64, 256, 1024, 4096])
+@pytest.mark.parametrize("T", list(SWEEP_T))
 def test_sweep_points(dev, T):
     cfg = sweep_config(T)
     u = Uploaded(make_inputs(cfg), dev)
