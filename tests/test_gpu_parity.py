@@ -615,6 +615,16 @@ def test_small_and_streaming_schedules_agree(dev, quant):
 
 
 # ------------------------------------------------------------------ binding checks
+def test_binding_stream_handle(dev):
+    """The binding launches on the stream torch reports as current: its raw handle lookup agrees
+    with torch.cuda.current_stream on the default stream and inside a side-stream context."""
+    assert F._stream(dev, None) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert F._stream(dev, None) == torch.cuda.current_stream(dev).cuda_stream == s.cuda_stream
+    assert F._stream(dev, s) == s.cuda_stream
+
+
 def test_binding_rejects_bad_output_buffers(dev):
     """Output buffers of the wrong shape, dtype or device are refused by the binding before
     the library is called (the library only sees pointers)."""

@@ -82,12 +82,22 @@ def select_variant(R: int, T: int, H: int, quant: bool) -> int:
     return _lib.farn_select_variant(R, T, H, int(bool(quant)))
 
 
+_BF16 = torch.bfloat16
+# The current stream's raw handle of a device, read without building a Stream object (the
+# public torch.cuda.current_stream costs about 2 us per call, this about 0.1 us).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_PTR_ARRAYS = [ctypes.c_void_p * n for n in range(MAX_R + 1)]
 
 
 def _ptr_array(ts):
-    arr = (ctypes.c_void_p * len(ts))()
+    n = len(ts)
+    arr = _PTR_ARRAYS[n]() if n <= MAX_R else (ctypes.c_void_p * n)()  # more than MAX_R: the library refuses it
     for i, t in enumerate(ts):
         arr[i] = t.data_ptr()
     return arr
@@ -102,10 +112,21 @@ def _device_of(t, name="partials[0]"):
 
 
 def _check_bf16(name, t, shape, device):
-    if t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) or not t.is_contiguous() \
-            or t.device != device:
+    if t.dtype is not _BF16 or t.shape != shape or not t.is_contiguous() or t.device != device:
         raise ValueError(f"{name}: expected contiguous bfloat16 {tuple(shape)} on {device}, "
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_inputs(partials, residual, gamma, shape, device):
+    """The partials, the residual (or None) and gamma: contiguous bf16 of the call's shape on
+    `device`. The common case is tested inline; a failure is reported by _check_bf16."""
+    for p in partials:
+        if p.dtype is not _BF16 or p.shape != shape or not p.is_contiguous() or p.device != device:
+            for i, q in enumerate(partials):
+                _check_bf16(f"partials[{i}]", q, shape, device)
+    if residual is not None:
+        _check_bf16("residual", residual, shape, device)
+    _check_bf16("gamma", gamma, shape[1:], device)
 
 
 def _check_buf(name, t, dtypes, numel, device):
@@ -116,13 +137,17 @@ def _check_buf(name, t, dtypes, numel, device):
 
 
 def _stream(device, stream):
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    """Raw hipStream_t (an int) of `stream`, or of the current stream of `device`."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _run(device, fn, *args):
     """Call into the library with `device` current (HIP launches on the current device)."""
-    if device.index is not None and device.index != torch.cuda.current_device():
+    if device.index != torch._C._cuda_getDevice():
         with torch.cuda.device(device):
             return fn(*args)
     return fn(*args)
@@ -134,17 +159,13 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
     residual (or None), round to bf16 -> residual_out, then RMSNorm with gamma -> out.
     residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
     p0 = partials[0]
-    T, H = p0.shape
+    T, H = shape = p0.shape
     dev = _device_of(p0)
-    for i, p in enumerate(partials):
-        _check_bf16(f"partials[{i}]", p, (T, H), dev)
-    if residual is not None:
-        _check_bf16("residual", residual, (T, H), dev)
-    _check_bf16("gamma", gamma, (H,), dev)
+    _check_inputs(partials, residual, gamma, shape, dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
     out = torch.empty_like(p0) if out is None else out
-    _check_bf16("residual_out", residual_out, (T, H), dev)
-    _check_bf16("out", out, (T, H), dev)
+    _check_bf16("residual_out", residual_out, shape, dev)
+    _check_bf16("out", out, shape, dev)
     st = _run(dev, _lib.farn_reduce_add_rmsnorm_ex,
               _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
               _ptr(residual_out), _ptr(out), _stream(dev, stream), variant)
@@ -161,21 +182,17 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
     (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128], or
     [H/128, T] with scales_col_major)."""
     p0 = partials[0]
-    T, H = p0.shape
+    T, H = shape = p0.shape
     dev = _device_of(p0)
-    for i, p in enumerate(partials):
-        _check_bf16(f"partials[{i}]", p, (T, H), dev)
-    if residual is not None:
-        _check_bf16("residual", residual, (T, H), dev)
-    _check_bf16("gamma", gamma, (H,), dev)
+    _check_inputs(partials, residual, gamma, shape, dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
-    _check_bf16("residual_out", residual_out, (T, H), dev)
+    _check_bf16("residual_out", residual_out, shape, dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
     if out is not None:
-        _check_bf16("out", out, (T, H), dev)
+        _check_bf16("out", out, shape, dev)
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
     G = H // group_size if group_size > 0 else 0
     if scales is None:
@@ -195,12 +212,12 @@ def reduce(partials, *, out=None, stream=None):
     """All-reduce alone (first kernel of the unfused compositions): bf16 of the fp32 rank-order
     sum of the partials. Returns out."""
     p0 = partials[0]
-    T, H = p0.shape
+    T, H = shape = p0.shape
     dev = _device_of(p0)
     for i, p in enumerate(partials):
-        _check_bf16(f"partials[{i}]", p, (T, H), dev)
+        _check_bf16(f"partials[{i}]", p, shape, dev)
     out = torch.empty_like(p0) if out is None else out
-    _check_bf16("out", out, (T, H), dev)
+    _check_bf16("out", out, shape, dev)
     st = _run(dev, _lib.farn_reduce, _ptr_array(partials), len(partials), T, H, _ptr(out),
               _stream(dev, stream))
     if st != OK:
@@ -210,9 +227,9 @@ def reduce(partials, *, out=None, stream=None):
 
 def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None):
     """Per-group E4M3 quant alone of a bf16 [T,H] tensor. Returns (q uint8 [T,H], scales fp32 [T,H/128])."""
-    T, H = x.shape
+    T, H = shape = x.shape
     dev = _device_of(x, "x")
-    _check_bf16("x", x, (T, H), dev)
+    _check_bf16("x", x, shape, dev)
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
     G = H // group_size if group_size > 0 else 0
     scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
@@ -232,21 +249,17 @@ def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, *, em
     E2M1 codes two per byte). Returns (residual_out, out or None, q uint8 [T, H/2],
     scales uint8 [T, H/32])."""
     p0 = partials[0]
-    T, H = p0.shape
+    T, H = shape = p0.shape
     dev = _device_of(p0)
-    for i, p in enumerate(partials):
-        _check_bf16(f"partials[{i}]", p, (T, H), dev)
-    if residual is not None:
-        _check_bf16("residual", residual, (T, H), dev)
-    _check_bf16("gamma", gamma, (H,), dev)
+    _check_inputs(partials, residual, gamma, shape, dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
-    _check_bf16("residual_out", residual_out, (T, H), dev)
+    _check_bf16("residual_out", residual_out, shape, dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
     if out is not None:
-        _check_bf16("out", out, (T, H), dev)
+        _check_bf16("out", out, shape, dev)
     q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev) if q is None else q
     scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None else scales
     _check_buf("q", q, (torch.uint8,), T * (H // 2), dev)
