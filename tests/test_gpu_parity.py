@@ -370,11 +370,24 @@ def test_graph_capture_replays_match_eager(dev):
     say("[gpu] graph capture")
     ua = Uploaded(make_inputs(CONFIGS["decode_ds"], seed=70), dev)
     ub = Uploaded(make_inputs(CONFIGS["decode_fp8"], seed=71), dev)
+    # a plain call large enough to take the launch with LDS reserved (two workgroups per CU)
+    uc = Uploaded(make_inputs(CONFIGS["prefill"], seed=72, R=6, T=2048, H=6152), dev)
     ea = F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS)
     eb = F.reduce_add_rmsnorm_quant_group(ub.P, ub.res, ub.g, EPS)
+    ec = F.reduce_add_rmsnorm(uc.P, uc.res, uc.g, EPS)
     torch.cuda.synchronize()
+    # the eager results themselves against the oracle
+    ra, rb = ua.oracle_rows(np.arange(ua.T), False), ub.oracle_rows(np.arange(ub.T), True)
+    rows_c = _sample_rows(uc.T, 24, seed=72)
+    rc = uc.oracle_rows(rows_c, False)
+    for (ro, out), r, rows in ((ea, ra, slice(None)), (eb[:2], rb, slice(None)), (ec, rc, rows_c)):
+        ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro)[rows], r[0]),
+                                   compare_bf16("out", from_dev_bf16(out)[rows], r[1]),
+                                   compare_fp8(eb[2].cpu().numpy(), rb[2], eb[3].cpu().numpy(), rb[3]) if r is rb else None)
+        assert ok, why
     ga = (torch.empty_like(ea[0]), torch.empty_like(ea[1]))
     gb = tuple(torch.empty_like(x) for x in eb)
+    gc = (torch.empty_like(ec[0]), torch.empty_like(ec[1]))
     # warm up on a side stream, as graph capture requires
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -387,13 +400,14 @@ def test_graph_capture_replays_match_eager(dev):
         F.reduce_add_rmsnorm(ua.P, ua.res, ua.g, EPS, residual_out=ga[0], out=ga[1])
         F.reduce_add_rmsnorm_quant_group(ub.P, ub.res, ub.g, EPS, residual_out=gb[0], out=gb[1],
                                          q=gb[2], scales=gb[3])
+        F.reduce_add_rmsnorm(uc.P, uc.res, uc.g, EPS, residual_out=gc[0], out=gc[1])
     for rep in range(4):
-        for t in ga + gb:
+        for t in ga + gb + gc:
             t.view(torch.uint8).fill_(0xA5)  # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for x, y in zip(ea + eb, ga + gb):
+        for x, y in zip(ea + eb + ec, ga + gb + gc):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {rep}"
 
 
@@ -512,6 +526,7 @@ def test_fp8_scales_column_major(dev, name):
     codes and bf16 outputs are unchanged."""
     u = Uploaded(make_inputs(CONFIGS[name], seed=95), dev)
     say(f"[gpu] column-major scales {name}")
+    r_ro, r_out, r_q, r_s = u.oracle_rows(np.arange(u.T), True)
     for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
         a = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant)
         b = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant, scales_col_major=True)
@@ -519,6 +534,11 @@ def test_fp8_scales_column_major(dev, name):
         for x, y in zip(a[:3], b[:3]):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
         assert b[3].shape == (u.H // 128, u.T) and torch.equal(a[3].t().contiguous(), b[3])
+        # against the oracle directly: its row-major scales, transposed
+        rep = compare_fp8(b[2].cpu().numpy(), r_q, b[3].cpu().numpy().T, r_s)
+        ok, why = within_tolerance(compare_bf16("residual_out", from_dev_bf16(b[0]), r_ro),
+                                   compare_bf16("out", from_dev_bf16(b[1]), r_out), rep)
+        assert ok, why
 
 
 def test_random_shapes(dev):
