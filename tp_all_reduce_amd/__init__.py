@@ -2,9 +2,11 @@
 quant) for MI355X (gfx950).
 
 Argument marshalling only: torch tensors supply device memory and the stream; every
-step of the op runs in the HIP kernels behind the C ABI (include/farn.h). Importing
-this package loads the in-tree library and raises if it has not been built; there
-is no fallback.
+step of the op runs in the HIP kernels behind the C ABI (include/farn.h). The tensor
+calls go through a small compiled extension (_farn_torch, from csrc/farn_torch.cpp)
+that checks every tensor and calls the C ABI's entry points; lib() gives the C ABI
+itself through ctypes. Importing this package loads both in-tree libraries and raises
+if either has not been built; there is no fallback.
 
 The op is the per-GPU body of the fused tensor-parallel all-reduce + RMSNorm of
 "ROCm AITER fused all-reduce + RMSNorm" (vLLM #37646 summary, fused_ar_rms) and of
@@ -87,53 +89,22 @@ _BF16 = torch.bfloat16
 # public torch.cuda.current_stream costs about 2 us per call, this about 0.1 us).
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
+try:
+    # tensor checks and pointer marshalling into the C ABI, compiled (csrc/farn_torch.cpp)
+    from . import _farn_torch as _ext
+except ImportError as e:
+    raise ImportError(f"{os.path.dirname(LIB_PATH)}/_farn_torch.so is not built or does not load ({e}); "
+                      "run `python tp_all_reduce_amd/build.py`. There is no fallback path.") from e
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
-
-
-_PTR_ARRAYS = [ctypes.c_void_p * n for n in range(MAX_R + 1)]
-
-
-def _ptr_array(ts):
-    n = len(ts)
-    arr = _PTR_ARRAYS[n]() if n <= MAX_R else (ctypes.c_void_p * n)()  # more than MAX_R: the library refuses it
-    for i, t in enumerate(ts):
-        arr[i] = t.data_ptr()
-    return arr
+_PLAIN, _FP8, _MXFP4 = 0, 1, 2
 
 
 def _device_of(t, name="partials[0]"):
     """The GPU the call runs on: that of its first input. The library takes plain pointers and
-    cannot tell host memory from device memory, so host tensors are refused here."""
-    if t.device.type != "cuda":
+    cannot tell host memory from device memory, so host tensors are refused."""
+    if not t.is_cuda:
         raise ValueError(f"{name}: expected a tensor on the GPU, got one on {t.device}")
     return t.device
-
-
-def _check_bf16(name, t, shape, device):
-    if t.dtype is not _BF16 or t.shape != shape or not t.is_contiguous() or t.device != device:
-        raise ValueError(f"{name}: expected contiguous bfloat16 {tuple(shape)} on {device}, "
-                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
-
-
-def _check_inputs(partials, residual, gamma, shape, device):
-    """The partials, the residual (or None) and gamma: contiguous bf16 of the call's shape on
-    `device`. The common case is tested inline; a failure is reported by _check_bf16."""
-    for p in partials:
-        if p.dtype is not _BF16 or p.shape != shape or not p.is_contiguous() or p.device != device:
-            for i, q in enumerate(partials):
-                _check_bf16(f"partials[{i}]", q, shape, device)
-    if residual is not None:
-        _check_bf16("residual", residual, shape, device)
-    _check_bf16("gamma", gamma, shape[1:], device)
-
-
-def _check_buf(name, t, dtypes, numel, device):
-    """A code or scale buffer: contiguous, of one of `dtypes`, `numel` elements, on `device`."""
-    if t.dtype not in dtypes or t.numel() != numel or not t.is_contiguous() or t.device != device:
-        raise ValueError(f"{name}: expected a contiguous {' / '.join(str(d) for d in dtypes)} tensor of "
-                         f"{numel} elements on {device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
 def _stream(device, stream):
@@ -145,30 +116,17 @@ def _stream(device, stream):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _run(device, fn, *args):
-    """Call into the library with `device` current (HIP launches on the current device)."""
-    if device.index != torch._C._cuda_getDevice():
-        with torch.cuda.device(device):
-            return fn(*args)
-    return fn(*args)
-
-
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual_out=None,
                        out=None, variant: int = VARIANT_AUTO, stream=None):
     """Sum the R partials (list of bf16 [T,H] device tensors) in rank order in fp32, add the
     residual (or None), round to bf16 -> residual_out, then RMSNorm with gamma -> out.
     residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
     p0 = partials[0]
-    T, H = shape = p0.shape
     dev = _device_of(p0)
-    _check_inputs(partials, residual, gamma, shape, dev)
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
     out = torch.empty_like(p0) if out is None else out
-    _check_bf16("residual_out", residual_out, shape, dev)
-    _check_bf16("out", out, shape, dev)
-    st = _run(dev, _lib.farn_reduce_add_rmsnorm_ex,
-              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
-              _ptr(residual_out), _ptr(out), _stream(dev, stream), variant)
+    st = _ext.fused(partials, residual, gamma, eps, residual_out, out, None, None, _PLAIN, 0, variant,
+                    _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm")
     return residual_out, out
@@ -182,27 +140,19 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
     (residual_out, out or None, q uint8 [T,H] E4M3 codes, scales float32 [T, H/128], or
     [H/128, T] with scales_col_major)."""
     p0 = partials[0]
-    T, H = shape = p0.shape
     dev = _device_of(p0)
-    _check_inputs(partials, residual, gamma, shape, dev)
+    T, H = p0.shape
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
-    _check_bf16("residual_out", residual_out, shape, dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
-    if out is not None:
-        _check_bf16("out", out, shape, dev)
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
-    G = H // group_size if group_size > 0 else 0
     if scales is None:
+        G = H // group_size if group_size > 0 else 0
         scales = torch.empty((G, T) if scales_col_major else (T, G), dtype=torch.float32, device=dev)
-    _check_buf("q", q, (torch.uint8, torch.float8_e4m3fn), T * H, dev)
-    _check_buf("scales", scales, (torch.float32,), T * G, dev)
-    st = _run(dev, _lib.farn_reduce_add_rmsnorm_quant_group_ex,
-              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H, group_size,
-              _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream),
-              variant | (SCALES_COL_MAJOR if scales_col_major else 0))
+    st = _ext.fused(partials, residual, gamma, eps, residual_out, out, q, scales, _FP8, group_size,
+                    variant | (SCALES_COL_MAJOR if scales_col_major else 0), _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_quant_group")
     return residual_out, out, q, scales
@@ -212,14 +162,9 @@ def reduce(partials, *, out=None, stream=None):
     """All-reduce alone (first kernel of the unfused compositions): bf16 of the fp32 rank-order
     sum of the partials. Returns out."""
     p0 = partials[0]
-    T, H = shape = p0.shape
     dev = _device_of(p0)
-    for i, p in enumerate(partials):
-        _check_bf16(f"partials[{i}]", p, shape, dev)
     out = torch.empty_like(p0) if out is None else out
-    _check_bf16("out", out, shape, dev)
-    st = _run(dev, _lib.farn_reduce, _ptr_array(partials), len(partials), T, H, _ptr(out),
-              _stream(dev, stream))
+    st = _ext.reduce(partials, out, _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce")
     return out
@@ -227,16 +172,12 @@ def reduce(partials, *, out=None, stream=None):
 
 def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None):
     """Per-group E4M3 quant alone of a bf16 [T,H] tensor. Returns (q uint8 [T,H], scales fp32 [T,H/128])."""
-    T, H = shape = x.shape
     dev = _device_of(x, "x")
-    _check_bf16("x", x, shape, dev)
+    T, H = x.shape
     q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
-    G = H // group_size if group_size > 0 else 0
-    scales = torch.empty((T, G), dtype=torch.float32, device=dev) if scales is None else scales
-    _check_buf("q", q, (torch.uint8, torch.float8_e4m3fn), T * H, dev)
-    _check_buf("scales", scales, (torch.float32,), T * G, dev)
-    st = _run(dev, _lib.farn_quant_group, _ptr(x), T, H, group_size, _ptr(q), _ptr(scales),
-              _stream(dev, stream))
+    if scales is None:
+        scales = torch.empty((T, H // group_size if group_size > 0 else 0), dtype=torch.float32, device=dev)
+    st = _ext.quant(x, group_size, q, scales, _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_quant_group")
     return q, scales
@@ -249,24 +190,17 @@ def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, *, em
     E2M1 codes two per byte). Returns (residual_out, out or None, q uint8 [T, H/2],
     scales uint8 [T, H/32])."""
     p0 = partials[0]
-    T, H = shape = p0.shape
     dev = _device_of(p0)
-    _check_inputs(partials, residual, gamma, shape, dev)
+    T, H = p0.shape
     residual_out = torch.empty_like(p0) if residual_out is None else residual_out
-    _check_bf16("residual_out", residual_out, shape, dev)
     if emit_out and out is None:
         out = torch.empty_like(p0)
     if not emit_out:
         out = None
-    if out is not None:
-        _check_bf16("out", out, shape, dev)
     q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev) if q is None else q
     scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None else scales
-    _check_buf("q", q, (torch.uint8,), T * (H // 2), dev)
-    _check_buf("scales", scales, (torch.uint8,), T * (H // MX_BLOCK), dev)
-    st = _run(dev, _lib.farn_reduce_add_rmsnorm_mxfp4_ex,
-              _ptr_array(partials), len(partials), _ptr(residual), _ptr(gamma), eps, T, H,
-              _ptr(residual_out), _ptr(out), _ptr(q), _ptr(scales), _stream(dev, stream), variant)
+    st = _ext.fused(partials, residual, gamma, eps, residual_out, out, q, scales, _MXFP4, 0, variant,
+                    _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce_add_rmsnorm_mxfp4")
     return residual_out, out, q, scales

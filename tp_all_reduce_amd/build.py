@@ -5,7 +5,9 @@
 (Run it by path: importing the package loads the built library.)
 
 The C-ABI layer (csrc/farn_api.cpp) makes no HIP call and is compiled by g++; the
-kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two. The plain C
+kernels (csrc/farn_kernels.hip) by hipcc for gfx950; hipcc links the two. The tensor-level
+Python binding (csrc/farn_torch.cpp -> _farn_torch.so) is compiled by g++ against torch's
+headers and links libfarn.so. The plain C
 client of the ABI that the GPU tests run (tests/c_abi_client.c) is compiled by gcc
 against include/farn.h and the built library, and the test kernels of the conversion
 instructions (tests/hw_conversions.hip) by hipcc.
@@ -22,6 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfarn.so")
+TORCH_BINDING = os.path.join(HERE, "_farn_torch.so")
 C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi_client.c")
 C_CLIENT = os.path.join(ROOT, "tests", "c_abi_client")
 HWCONV_SRC = os.path.join(ROOT, "tests", "hw_conversions.hip")
@@ -59,6 +62,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + f".tmp{os.getpid()}"
     out += _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, api_o, ker_o])
     os.replace(tmp, LIB)
+    out += build_torch_binding()
     out += build_c_client()
     out += build_hwconv()
     if verbose:
@@ -76,6 +80,30 @@ def build_c_client() -> list:
                 f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../tp_all_reduce_amd",
                 f"-Wl,-rpath,{ROCM}/lib"])
     os.replace(tmp, C_CLIENT)
+    return out
+
+
+def build_torch_binding() -> list:
+    """The tensor-level Python binding (csrc/farn_torch.cpp): a torch C++ extension compiled
+    by g++ against torch's headers, linked to libfarn.so (found next to it through the
+    rpath) and to the torch libraries the importing process has already loaded."""
+    import sysconfig
+
+    import torch
+    from torch.utils import cpp_extension
+
+    tmp = TORCH_BINDING + f".tmp{os.getpid()}"
+    abi = int(torch._C._GLIBCXX_USE_CXX11_ABI)
+    cmd = ["g++", *CXX_FLAGS, "-shared", f"-D_GLIBCXX_USE_CXX11_ABI={abi}",
+           "-DTORCH_EXTENSION_NAME=_farn_torch", "-DTORCH_API_INCLUDE_EXTENSION_H",
+           *[f"-I{p}" for p in cpp_extension.include_paths()], f"-I{sysconfig.get_paths()['include']}",
+           os.path.join(CSRC, "farn_torch.cpp"), "-o", tmp,
+           *[f"-L{p}" for p in cpp_extension.library_paths()], "-lc10", "-ltorch", "-ltorch_cpu",
+           "-ltorch_python", f"-L{HERE}", "-lfarn", "-Wl,-rpath,$ORIGIN"]
+    # torch's own headers trip -Wextra's unused-parameter warning; the binding's code does not
+    cmd.append("-Wno-unused-parameter")
+    out = _run(cmd)
+    os.replace(tmp, TORCH_BINDING)
     return out
 
 
