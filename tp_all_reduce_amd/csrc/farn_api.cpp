@@ -154,7 +154,9 @@ int select(int R, int64_t T, int64_t H, int quant) {
 // per compute unit) leaves room for only two. Measured on MI355X (median of 5, interleaved,
 // eager back-to-back calls): R = 8, H = 7168: -2.9 % at T = 2048, -2.3 % at T = 4096, -1.9 %
 // at T = 8192 (205.4 -> 201.4 us); R = 8, H = 6656: -3.9 % at T = 2048; R = 7: -1.7 .. -2.0 %
-// and R = 6: -0.6 .. -1.3 % at T = 8192. No change at T <= 1024 (R = 8) and for the FP8 and
+// and R = 6: -0.6 .. -1.3 % at T = 8192; at the rule's edges (R = 6, 7 at T = 2048, 4096;
+// H = 6152) -0.4 .. -6.1 %, in two placements of the arrays in memory each, and -1.6 .. -2.4 %
+// over six placements at R = 8, T = 8192. No change at T <= 1024 (R = 8) and for the FP8 and
 // MXFP4 calls (register-bound to about two already); slower with fewer ranks (R = 5: +1 ..
 // +3 %, R = 4: +1.9 %, R = 2: +4.6 %) and no gain at H = 8192.
 constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
