@@ -1,18 +1,21 @@
 """Bench of the fused reduce + residual-add + RMSNorm (+ FP8 group-128 quant) op on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--variant V]
-                    [--cpu-budget S] [--no-secondary] [--sweep]
+                    [--kernels 1|2|3] [--cpu-budget S] [--no-secondary] [--no-sweep]
 
 A step is one call of the FP8 entry point (reduce, residual add, bf16 round,
 RMSNorm, per-group E4M3 quant, size-based dispatch) over one batch already resident
-in HBM. The default workload is the prefill chunk R=8, T=8192, H=7168 with the bf16
+in HBM (with --kernels 2 or 3, the same step as the two- or three-kernel composition
+the fused call replaces). The default workload is the prefill chunk R=8, T=8192, H=7168 with the bf16
 output emitted: 1,352,400,896 algorithmic bytes per call, well beyond the 256 MB
 Infinity Cache, so every call streams from HBM.
 
 Prints ONE JSON line: value = algorithmic bytes per step / time per step (GB/s), with
 the roofline of the kernel (HBM bound, 8 TB/s peak), the CPU oracle timed on host
 cores on the same workload (its last pass also checks every output of the timed GPU
-call: the parity field), and secondary figures for the decode shapes (us/call).
+call: the parity field), the message-size sweep (R=8, H=8192, T=2..4096: us/call and
+GB/s, cache-hot and streaming from HBM), and secondary figures for the decode shapes
+(us/call).
 """
 
 from __future__ import annotations
@@ -79,6 +82,7 @@ class Bufs:
         self.res = to_dev_bf16(d["residual"], dev)
         self.g = to_dev_bf16(d["gamma"], dev)
         self.quant, self.emit_out = quant, emit_out
+        self.kernels = 1  # 2 or 3: call() runs the unfused composition of the FP8 step
         self.alloc_outputs(dev)
 
     def alloc_outputs(self, dev):
@@ -95,6 +99,7 @@ class Bufs:
     def clone(self, dev):
         c = object.__new__(Bufs)
         c.R, c.T, c.H, c.quant, c.emit_out = self.R, self.T, self.H, self.quant, self.emit_out
+        c.kernels = self.kernels
         c.P = [p.clone() for p in self.P]
         c.res, c.g = self.res.clone(), self.g.clone()
         c.alloc_outputs(dev)
@@ -116,6 +121,10 @@ class Bufs:
         F.quant_group(self.out, q=self.q, scales=self.s)
 
     def call(self, variant):
+        if self.kernels == 2:
+            return self.call_2kernel(variant)
+        if self.kernels == 3:
+            return self.call_3kernel(variant)
         if self.quant == "mxfp4":
             F.reduce_add_rmsnorm_mxfp4(self.P, self.res, self.g, 1e-6, emit_out=self.emit_out,
                                        residual_out=self.ro, out=self.out, q=self.q, scales=self.s,
@@ -215,7 +224,7 @@ def cpu_baseline(d, cfg, quant, emit_out, budget_s, bufs=None):
     last pass's outputs are also compared with the GPU's over every row: returns
     (baseline, parity report or None)."""
     import oracle
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads, affinity, share = oracle_threads()
     passes, spent, ref = 0, 0.0, None
     while spent < budget_s:
         t0 = time.perf_counter()
@@ -241,12 +250,30 @@ def cpu_baseline(d, cfg, quant, emit_out, budget_s, bufs=None):
     else:
         oracle.reduce_add_rmsnorm(P1, r1, d["gamma"], 1e-6, nthreads=1)
     one = time.perf_counter() - t0
-    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    if bufs is not None and bufs.kernels == 3:
+        # the three-kernel composition rounds the all-reduce to bf16 before the residual add:
+        # its reference is the oracle's composition of the same three blocks
+        ar = oracle.reduce(d["partials"])
+        r_ro, r_out = oracle.reduce_add_rmsnorm(ar[None], d["residual"], d["gamma"], 1e-6, nthreads=threads)
+        ref = (r_ro, r_out) + oracle.quant_group(r_out)
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": threads, "threads": threads,
+            "cores_in_affinity_mask": affinity, "cpu_share": share, "kind": "oracle",
             "sample": f"{passes} full pass(es) over the workload ({cfg.T} rows), {spent:.1f} s",
             "ms_per_call": round(spent / passes * 1e3, 2),
             "one_thread": {"GBps": round(nbytes(cfg, quant, emit_out) * rows / cfg.T / one / 1e9, 3),
                            "sample": f"{rows} rows, {one:.2f} s"},
             "cpu_model": cpu_model()}, (None if bufs is None else parity_report(ref, bufs, quant, emit_out))
+
+
+def oracle_threads():
+    """Threads for the oracle: every core in this process's affinity mask, capped at the CPU
+    share the environment states (OMP_NUM_THREADS, when set), since a shared host's mask can
+    list more cores than this process is meant to use. Returns (threads, cores in the mask,
+    the stated share or None)."""
+    affinity = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    share = int(share) if share and share.isdigit() and int(share) > 0 else None
+    return (min(affinity, share) if share else affinity), affinity, share
 
 
 def cpu_model():
@@ -369,7 +396,10 @@ def sweep(dev):
     replay: hot (one buffer set, cache-resident) and cold (sets rotated over >= 1 GiB, so every
     call streams from HBM rather than the 256 MB last-level cache), with the cold rate, and
     both launch shapes forced (hot) beside the one the dispatch rule picks."""
-    out = {}
+    out = {"what": "R=8, H=8192, plain call, shape chosen by the dispatch rule; graph replay, median of 3; "
+                   "hot = one buffer set (cache-resident), cold = sets rotated over >= 1 GiB (streams from HBM); "
+                   "forced_hot_us = both launch shapes forced, hot",
+           "peak_GBps": PEAK_HBM_GBPS, "points": []}
     for T in SWEEP_T:
         cfg = sweep_config(T)
         b = Bufs(make_inputs(cfg), dev, False, True)
@@ -384,12 +414,12 @@ def sweep(dev):
         calls = k * max(1, 200 // k)
         cold = median_graph(sets, F.VARIANT_AUTO, calls, max(2, 2000 // calls))
         gbps = nb / (cold * 1e-3) / 1e9
-        out[f"T{T}"] = {"us_per_call_graph_hot": round(hot * 1e3, 2), "us_per_call_graph_cold": round(cold * 1e3, 2),
-                        "GBps_graph_cold": round(gbps, 1), "pct_of_peak_cold": round(100 * gbps / PEAK_HBM_GBPS, 1),
-                        "rotation_sets": k, "bytes_per_call": nb,
-                        "variant": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)],
-                        "forced_hot_us": forced}
-        log(f"sweep T={T}: {out[f'T{T}']}")
+        pt = {"T": T, "bytes": nb, "hot_us": round(hot * 1e3, 2), "cold_us": round(cold * 1e3, 2),
+              "cold_GBps": round(gbps, 1), "cold_pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
+              "shape": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)],
+              "forced_hot_us": forced, "rotation_sets": k}
+        out["points"].append(pt)
+        log(f"sweep T={T}: {pt}")
         del sets, b
         torch.cuda.empty_cache()
     return out
@@ -431,8 +461,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the message-size sweep (R=8, H=8192, T=2..4096), hot and cache-cold")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the message-size sweep (R=8, H=8192, T=2..4096), hot and cache-cold")
+    ap.add_argument("--kernels", type=int, default=1, choices=(1, 2, 3),
+                    help="time the FP8 step as the fused call (1), fused AR+RMSNorm then the quant (2), "
+                         "or all-reduce, add+RMSNorm, quant (3); FP8 workloads only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one torch copy of 1 GiB (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -447,10 +480,14 @@ def main():
     dev = torch.device("cuda:0")
     cfg, quant, emit_out = WORKLOADS[args.workload]
     variant = VARIANT_NAMES[args.variant]
+    if args.kernels != 1 and not (quant is True and emit_out):
+        print("--kernels 2/3 time the FP8 step with the bf16 output: pick an FP8 workload", file=sys.stderr)
+        sys.exit(2)
 
     log(f"generating {args.workload}")
     d = make_inputs(cfg)
     bufs = Bufs(d, dev, quant, emit_out)
+    bufs.kernels = args.kernels
     nb = nbytes(cfg, quant, emit_out)
 
     if args.copy_calibration:
@@ -474,7 +511,7 @@ def main():
     ms, wall_ms = time_calls([bufs], variant, args.steps, args.warmup)
     gbps = nb / (ms * 1e-3) / 1e9
     ran = F.select_variant(cfg.R, cfg.T, cfg.H, quant) if variant == F.VARIANT_AUTO else variant
-    traffic = recorded_traffic(args.workload)
+    traffic = recorded_traffic(args.workload) if args.kernels == 1 else None
     result = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -483,14 +520,20 @@ def main():
         "config": {"workload": describe(cfg, quant, emit_out), "name": args.workload, "R": cfg.R,
                    "T": cfg.T, "H": cfg.H, "quant": quant, "emit_bf16_out": emit_out,
                    "variant": {1: "latency", 2: "bandwidth"}[ran], "bytes_per_step": nb,
-                   "seed": cfg.seed},
+                   "kernels_per_step": args.kernels, "seed": cfg.seed},
         "us_per_call": round(ms * 1e3, 2), "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
         "settle_calls": settle_calls,
         "wall_us_per_call": round(wall_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1),
-                     "kernel": "farn_rows (" + {1: "latency", 2: "bandwidth"}[ran] + " shape)",
+                     "traffic_source": None if traffic is None else (
+                         "recorded rocprofv3 FETCH_SIZE + WRITE_SIZE counters of this kernel source (sha256[:16] "
+                         f"{kernel_hash()}), scaled by a 1 GiB copy, in profiles/traffic.json; HBM bytes per "
+                         "launch / this run's time per launch"),
+                     "kernel": "farn_rows (" + {1: "latency", 2: "bandwidth"}[ran] + " shape)"
+                               + ("" if args.kernels == 1 else f" + {args.kernels - 1} unfused kernel(s)"),
+                     "kernel_sha": kernel_hash(),
                      "algorithmic_bytes_per_launch": nb,
                      "hbm_bytes_per_launch": traffic},
         "parity": None,
@@ -513,9 +556,9 @@ def main():
         result["secondary"] = secondary(dev, 200)
         log("unfused compositions")
         result["secondary"]["unfused_fp8"] = unfused(dev)
-    if args.sweep:
+    if not args.no_sweep:
         log("message-size sweep")
-        result.setdefault("secondary", {})["sweep_R8_H8192"] = sweep(dev)
+        result["sweep"] = sweep(dev)
     print(json.dumps(result), flush=True)
 
 

@@ -33,6 +33,38 @@ def build(force: bool = False) -> str:
 
 
 _lib = None
+# Thread count the fused-call wrappers use when none is given, and whether they fill their
+# outputs with a pattern before the call (so that an element the C code never writes shows
+# up as a wrong value rather than as whatever the allocator left there). `threads()` sets
+# both for a block of code.
+_default_threads = 1
+_poison = False
+_POISON_BYTE = 0xA5
+
+
+@contextlib.contextmanager
+def threads(n: int, poison: bool = True):
+    """Run the fused-call wrappers with `n` threads (rows dealt round-robin to the threads)
+    unless a call names its own count, with poisoned outputs. The pins use it to run the
+    checks on the threaded row split."""
+    global _default_threads, _poison
+    saved = (_default_threads, _poison)
+    _default_threads, _poison = int(n), bool(poison)
+    try:
+        yield
+    finally:
+        _default_threads, _poison = saved
+
+
+def _nthreads(n):
+    return _default_threads if n is None else int(n)
+
+
+def _out(shape, dtype):
+    a = np.empty(shape, dtype)
+    if _poison:
+        a.view(np.uint8).fill(_POISON_BYTE)
+    return a
 
 
 def _bind(L: ctypes.CDLL) -> ctypes.CDLL:
@@ -114,7 +146,7 @@ def _ptr_array(plist):
     return arr
 
 
-def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, nthreads: int = 1,
+def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, nthreads: int | None = None,
                        in_place: bool = False):
     """Plain call. partials: [R,T,H] (or list of [T,H]) uint16 bf16 bits; residual [T,H]
     uint16 or None; gamma [H] uint16. Returns (residual_out, out) as uint16 arrays.
@@ -122,38 +154,38 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, nthreads: i
     plist = _partials_list(partials)
     T, H = plist[0].shape
     g = np.ascontiguousarray(gamma, dtype=np.uint16)
-    out = np.empty((T, H), np.uint16)
+    out = _out((T, H), np.uint16)
     if in_place:
         res = np.array(residual, dtype=np.uint16, copy=True)
         res_out = res
     else:
         res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
-        res_out = np.empty((T, H), np.uint16)
+        res_out = _out((T, H), np.uint16)
     rc = lib().oracle_reduce_add_rmsnorm(
         _ptr_array(plist), len(plist), None if res is None else _u16(res), _u16(g), eps, T, H,
-        _u16(res_out), _u16(out), nthreads)
+        _u16(res_out), _u16(out), _nthreads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_reduce_add_rmsnorm failed ({rc})")
     return res_out, out
 
 
 def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6, group: int = 128,
-                                   emit_out: bool = True, nthreads: int = 1):
+                                   emit_out: bool = True, nthreads: int | None = None):
     """FP8 call. Returns (residual_out [T,H] u16, out [T,H] u16 or None, q [T,H] u8 e4m3fn codes,
     scales [T, H/group] float32)."""
     plist = _partials_list(partials)
     T, H = plist[0].shape
     g = np.ascontiguousarray(gamma, dtype=np.uint16)
     res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
-    res_out = np.empty((T, H), np.uint16)
-    out = np.empty((T, H), np.uint16) if emit_out else None
-    q = np.empty((T, H), np.uint8)
-    scales = np.empty((T, H // group), np.float32)
+    res_out = _out((T, H), np.uint16)
+    out = _out((T, H), np.uint16) if emit_out else None
+    q = _out((T, H), np.uint8)
+    scales = _out((T, H // group), np.float32)
     rc = lib().oracle_reduce_add_rmsnorm_quant_group(
         _ptr_array(plist), len(plist), None if res is None else _u16(res), _u16(g), eps, T, H, group,
         _u16(res_out), None if out is None else _u16(out),
         q.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
-        scales.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), nthreads)
+        scales.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _nthreads(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_reduce_add_rmsnorm_quant_group failed ({rc})")
     return res_out, out, q, scales
@@ -231,20 +263,21 @@ def mxfp4(x):
 
 
 def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, emit_out: bool = True,
-                             nthreads: int = 1):
+                             nthreads: int | None = None):
     """Fused call with MXFP4 output: (residual_out, out or None, q [T,H/2] u8, scales [T,H/32] u8)."""
     plist = _partials_list(partials)
     T, H = plist[0].shape
     g = np.ascontiguousarray(gamma, dtype=np.uint16)
     res = None if residual is None else np.ascontiguousarray(residual, dtype=np.uint16)
-    res_out = np.empty((T, H), np.uint16)
-    out = np.empty((T, H), np.uint16) if emit_out else None
-    q = np.empty((T, H // 2), np.uint8)
-    sc = np.empty((T, H // 32), np.uint8)
+    res_out = _out((T, H), np.uint16)
+    out = _out((T, H), np.uint16) if emit_out else None
+    q = _out((T, H // 2), np.uint8)
+    sc = _out((T, H // 32), np.uint8)
     u8 = ctypes.POINTER(ctypes.c_uint8)
     rc = lib().oracle_reduce_add_rmsnorm_mxfp4(
         _ptr_array(plist), len(plist), None if res is None else _u16(res), _u16(g), eps, T, H,
-        _u16(res_out), None if out is None else _u16(out), q.ctypes.data_as(u8), sc.ctypes.data_as(u8), nthreads)
+        _u16(res_out), None if out is None else _u16(out), q.ctypes.data_as(u8), sc.ctypes.data_as(u8),
+        _nthreads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_reduce_add_rmsnorm_mxfp4 failed")
     return res_out, out, q, sc

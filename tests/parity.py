@@ -8,7 +8,9 @@ Tolerances (the op's statement of parity):
   * E4M3 codes: at most 0.1% of codes may differ, each by one code (adjacent magnitude,
     same sign).
   * fp32 scales: relative error <= 1e-3.
-NaN compares equal to NaN; +0 equals -0.
+NaN compares equal to NaN. Signed zeros must match: a +0 against a -0 (bf16 0x0000 / 0x8000,
+E4M3 code 0x00 / 0x80, E2M1 code 0x0 / 0x8) counts as a bit or code difference (numerically it
+is within every tolerance).
 """
 
 from __future__ import annotations
@@ -45,7 +47,7 @@ def compare_bf16(name: str, gpu_bits, ref_bits) -> dict:
     with np.errstate(invalid="ignore"):
         tol = BF16_REL * np.abs(r) + BF16_ABS
         bad = ~(err <= tol) & ~both_nan  # a NaN reference has a NaN tolerance
-    ne = (gpu_bits != ref_bits) & ~both_nan & ~((g == 0) & (r == 0))
+    ne = (gpu_bits != ref_bits) & ~both_nan
     with np.errstate(invalid="ignore"):
         rel = np.where(np.abs(r) > 0, err / np.maximum(np.abs(r), 1e-30), err)
     return {"name": name, "n": int(g.size), "n_bad": int(bad.sum()), "n_bit_diff": int(ne.sum()),
@@ -63,11 +65,8 @@ def _code_rank(c: np.ndarray) -> np.ndarray:
 
 def compare_fp8(gpu_q, ref_q, gpu_s, ref_s) -> dict:
     gq, rq = np.asarray(gpu_q, np.uint8), np.asarray(ref_q, np.uint8)
-    zero_g = (gq & 0x7F) == 0
-    zero_r = (rq & 0x7F) == 0
-    diff = (gq != rq) & ~(zero_g & zero_r)
+    diff = gq != rq  # 0x00 against 0x80 counts (step 0: the same value)
     step = np.abs(_code_rank(gq) - _code_rank(rq))
-    step = np.where(zero_g & zero_r, 0, step)
     gs, rs = np.asarray(gpu_s, np.float64), np.asarray(ref_s, np.float64)
     s_nan = np.isnan(gs) & np.isnan(rs)
     s_err = np.where(s_nan, 0.0, np.abs(gs - rs) / np.where(rs != 0, np.abs(rs), 1.0))
@@ -105,9 +104,8 @@ def compare_mxfp4(gpu_q, ref_q, gpu_s, ref_s) -> dict:
     g = np.stack([gq & 0xF, gq >> 4], axis=-1).reshape(-1).astype(np.int32)
     r = np.stack([rq & 0xF, rq >> 4], axis=-1).reshape(-1).astype(np.int32)
     rank = lambda c: np.where(c & 0x8, -(c & 0x7), c & 0x7)
-    zero = ((g & 0x7) == 0) & ((r & 0x7) == 0)
-    diff = (g != r) & ~zero
-    step = np.where(zero, 0, np.abs(rank(g) - rank(r)))
+    diff = g != r  # 0x0 against 0x8 counts (step 0: the same value)
+    step = np.abs(rank(g) - rank(r))
     gs, rs = np.asarray(gpu_s, np.int32), np.asarray(ref_s, np.int32)
     sdiff = gs != rs
     return {"n": int(g.size), "n_code_diff": int(diff.sum()), "frac_code_diff": float(diff.mean()) if g.size else 0.0,

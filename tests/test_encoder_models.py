@@ -1,10 +1,11 @@
 """Exhaustive CPU check of the arithmetic the FP8 kernel does before its conversion
 instruction: the binary32 quotient o / scale computed without a divide (`fp32_quotient` in
-tp_all_reduce_amd/csrc/farn_kernels.hip: q0 = o*inv, r = o - q0*scale by FMA, q0 + r*inv by
-FMA; with `quant_slot`'s per-group scale, 2^64 rescaling of tiny groups and clamped remainder
+tp_all_reduce_amd/csrc/farn_kernels.hip: q0 = o*inv, the negated remainder nr = q0*scale - o by
+FMA, q0 - nr*inv by FMA; with `quant_slot`'s per-group scale, 2^64 rescaling of tiny groups and clamped remainder
 scale). That quotient can differ from the correctly rounded one by an fp32 unit; this test
 shows that its round-to-nearest-even E4M3 code never does, for every finite bf16 value each
-group can hold, over ~3,300 group maxima (every bf16 subnormal amax included). The conversion
+group can hold, over ~3,300 group maxima (every bf16 subnormal amax included), signed zeros
+included (a -0 value keeps the -0 code 0x80 the division gives). The conversion
 instruction's own rounding is checked on the GPU (tests/test_gpu_conversions.py); here it is
 the oracle's E4M3 encoder. A model is only as faithful as its transcription: a change to
 `fp32_quotient` or to `quant_slot`'s per-group arithmetic must be repeated here.
@@ -49,8 +50,8 @@ def quotient_model(o: np.ndarray, scale_r: np.float32, inv: np.float32) -> np.nd
     o = np.asarray(o, np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         q0 = (o * F32(inv)).astype(np.float32)
-        r = _fma32(-q0, np.full_like(q0, scale_r), o)
-        return _fma32(r, np.full_like(q0, inv), q0)
+        nr = _fma32(q0, np.full_like(q0, scale_r), -o)
+        return _fma32(-nr, np.full_like(q0, inv), q0)
 
 
 def group_codes_model(o: np.ndarray, amax: np.float32) -> tuple[np.ndarray, np.float32]:
@@ -91,8 +92,7 @@ def _check_groups(amax_patterns: np.ndarray) -> int:
         with np.errstate(divide="ignore"):
             v32 = (o / scale).astype(np.float32)              # IEEE single division
         want = oracle.e4m3fn_from_double_array(v32.astype(np.float64))
-        # signed zeros compare numerically: the correction step turns a -0 quotient into +0
-        bad = np.nonzero((got != want) & ~(((got & 0x7F) == 0) & ((want & 0x7F) == 0)))[0]
+        bad = np.nonzero(got != want)[0]  # bit for bit, signed zeros included
         assert bad.size == 0, (f"amax {amax!r}: o={o[bad[0]]!r} model {got[bad[0]]:#x} "
                                f"binary32 quotient's code {want[bad[0]]:#x} ({bad.size} differ)")
         checked += o.size
@@ -113,6 +113,9 @@ def test_quotient_codes_every_amax():
 
 
 def test_quotient_model_specials():
+    # -0 keeps its sign through the correction (code 0x80, as -0 / scale gives), +0 stays +0
+    codes, _ = group_codes_model(np.array([-0.0, 0.0, -1.0, 1.0], np.float32), F32(1.0))
+    assert codes.tolist()[:2] == [0x80, 0x00]
     # an all-zero group: scale 0, inv 0, quotients +-0 (the kernel masks their signs)
     codes, scale = group_codes_model(np.array([0.0, -0.0], np.float32), F32(0.0))
     assert scale == 0 and (codes & 0x7F).tolist() == [0, 0]

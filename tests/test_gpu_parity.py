@@ -1,14 +1,16 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, element by element,
 on the same seeded bf16 inputs, at the tolerances stated in tests/parity.py.
 
-Small configurations are compared whole. The full-size prefill chunk (R=8, T=8192,
-H=7168) and the large sweep points are run whole on the GPU, in the launch
-configuration the bench times, and compared on sampled rows (the oracle computes
-rows independently), plus whole-tensor properties.
+Every configuration is compared whole, every row and every element: the full-size prefill
+chunk (R=8, T=8192, H=7168) in the launch configuration the bench times, with and without
+FP8 and with MXFP4 output, and every point of the message-size sweep (R=8, H=8192,
+T=2..4096). The oracle runs threaded (rows dealt to the host's cores); its threaded row
+split is pinned on the CPU like the rest of it.
 """
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -24,6 +26,8 @@ from parity import (compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16, mxf
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
 VARIANTS = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
+# oracle threads: the host cores this process may run on, at most 16
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def say(msg):
@@ -48,15 +52,17 @@ class Uploaded:
 
     def oracle_rows(self, rows, quant, emit_out=True, residual=True):
         d = self.d
-        P = d["partials"][:, rows, :]
-        res = d["residual"][rows] if (residual and self.res is not None) else None
+        every = len(rows) == self.T and np.array_equal(rows, np.arange(self.T))
+        P = d["partials"] if every else d["partials"][:, rows, :]
+        res = (d["residual"] if every else d["residual"][rows]) if (residual and self.res is not None) else None
         if quant:
-            return oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], EPS, 128, emit_out, nthreads=8)
-        return oracle.reduce_add_rmsnorm(P, res, d["gamma"], EPS, nthreads=8)
+            return oracle.reduce_add_rmsnorm_quant_group(P, res, d["gamma"], EPS, 128, emit_out,
+                                                         nthreads=ORACLE_THREADS)
+        return oracle.reduce_add_rmsnorm(P, res, d["gamma"], EPS, nthreads=ORACLE_THREADS)
 
 
 def run_and_compare(u: Uploaded, quant: bool, variant: str = "auto",
-                    emit_out: bool = True, rows=None, label: str = ""):
+                    emit_out: bool = True, rows=None, label: str = "", ref=None):
     say(f"[gpu] {label} R={u.R} T={u.T} H={u.H} quant={quant} variant={variant} "
         f"emit={emit_out} residual={u.res is not None}")
     if quant:
@@ -68,7 +74,8 @@ def run_and_compare(u: Uploaded, quant: bool, variant: str = "auto",
     rows = np.arange(u.T) if rows is None else np.asarray(rows)
     g_ro = from_dev_bf16(ro)[rows]
     g_out = from_dev_bf16(out)[rows] if out is not None else None
-    ref = u.oracle_rows(rows, quant, emit_out)
+    if ref is None:
+        ref = u.oracle_rows(rows, quant, emit_out)
     rep_ro = compare_bf16("residual_out", g_ro, ref[0])
     rep_out = compare_bf16("out", g_out, ref[1]) if g_out is not None else None
     rep_fp8 = None
@@ -94,24 +101,32 @@ def test_configs_small(dev, name, variant):
         run_and_compare(u, True, variant, label=name + "+fp8")
 
 
-def _sample_rows(T, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    edge = [0, 1, 2, T // 2, T - 2, T - 1, 255, 256, 257, 511, 512, 1023, 1024]
-    rows = set(r for r in edge if 0 <= r < T) | set(rng.integers(0, T, n).tolist())
-    return np.array(sorted(rows))
-
-
 @pytest.fixture(scope="module")
 def prefill(dev):
     say("[gpu] generating prefill chunk R=8 T=8192 H=7168")
-    return Uploaded(make_inputs(CONFIGS["prefill"]), dev)
+    u = Uploaded(make_inputs(CONFIGS["prefill"]), dev)
+    u.refs = {}  # the oracle's outputs over every row, per call kind, computed once
+    return u
+
+
+def _prefill_ref(u, kind):
+    if kind not in u.refs:
+        say(f"[gpu] oracle over all {u.T} rows ({kind}, {ORACLE_THREADS} threads)")
+        d = u.d
+        if kind == "mxfp4":
+            u.refs[kind] = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS,
+                                                           nthreads=ORACLE_THREADS)
+        else:
+            u.refs[kind] = u.oracle_rows(np.arange(u.T), kind == "fp8")
+    return u.refs[kind]
 
 
 @pytest.mark.parametrize("quant", [False, True])
 @pytest.mark.parametrize("variant", ["auto", "latency", "bandwidth"])
-def test_prefill_full_size_sampled(prefill, quant, variant):
-    rows = _sample_rows(prefill.T)
-    run_and_compare(prefill, quant, variant, rows=rows, label="prefill")
+def test_prefill_full_size_all_rows(prefill, quant, variant):
+    rep = run_and_compare(prefill, quant, variant, label="prefill, every row",
+                          ref=_prefill_ref(prefill, "fp8" if quant else "plain"))
+    say(f"[gpu]   {rep}")
 
 
 def test_prefill_full_size_properties(prefill):
@@ -133,12 +148,12 @@ def test_prefill_full_size_properties(prefill):
 def test_two_workgroups_per_cu_launch(dev, R, H):
     """The plain call's bandwidth shape at H = 6152..7168 with R >= 6 and T >= 2048 is launched
     with LDS reserved so that at most two workgroups share a compute unit: its outputs match the
-    oracle on sampled rows, and the latency shape (launched without the reservation) bit for bit
+    oracle on every row, and the latency shape (launched without the reservation) bit for bit
     on every row."""
     T = 2048
     u = Uploaded(make_inputs(CONFIGS["prefill"], seed=40 + R, R=R, T=T, H=H), dev)
     assert F.select_variant(R, T, H, False) == F.VARIANT_BANDWIDTH
-    run_and_compare(u, False, "auto", rows=_sample_rows(T, 32, seed=R), label="two-per-CU")
+    run_and_compare(u, False, "auto", label="two-per-CU")
     a = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_BANDWIDTH)
     b = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_LATENCY)
     torch.cuda.synchronize()
@@ -148,11 +163,12 @@ def test_two_workgroups_per_cu_launch(dev, R, H):
 
 @pytest.mark.parametrize("T", list(SWEEP_T))
 def test_sweep_points(dev, T):
+    """Every row of every message-size sweep point, in every launch shape."""
     cfg = sweep_config(T)
     u = Uploaded(make_inputs(cfg), dev)
-    rows = None if T <= 256 else _sample_rows(T, 32, seed=T)
+    ref = u.oracle_rows(np.arange(T), False)
     for variant in VARIANTS:
-        run_and_compare(u, False, variant, rows=rows, label=cfg.name)
+        run_and_compare(u, False, variant, label=cfg.name, ref=ref)
 
 
 # ------------------------------------------------------------------ edge shapes
@@ -362,6 +378,38 @@ def test_nan_row(dev):
     assert ok, why
 
 
+def test_signed_zeros_bit_exact(dev):
+    """Elements whose sum is -0 (every partial and the residual -0) give residual_out = out =
+    -0 and the -0 codes (E4M3 0x80, E2M1 0x8), as the oracle's division and encoders give;
+    tiny negative values beside a large group maximum round to the -0 code too. Every output
+    must equal the oracle bit for bit, in both launch shapes."""
+    d = make_inputs(CONFIGS["tiny"], seed=61, R=3, T=5, H=1024)
+    P, res = d["partials"], d["residual"]
+    for t in range(5):
+        cols = np.arange(t, 1024, 7 + t)
+        P[:, t, cols] = 0x8000
+        res[t, cols] = 0x8000
+    # row 4: one large value per group, the rest tiny negatives (quotients far below 2^-10)
+    P[:, 4, :] = 0x8000
+    res[4, :] = 0xB000            # -4.7e-10
+    res[4, ::128] = 0x4300        # 128.0
+    u = Uploaded(d, dev)
+    ref = u.oracle_rows(np.arange(5), True)
+    ref_mx = oracle.reduce_add_rmsnorm_mxfp4(P, res, d["gamma"], EPS, nthreads=4)
+    assert (ref[1] == 0x8000).sum() >= 400 and (ref[2][4] == 0x80).sum() >= 1000
+    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+        say(f"[gpu] signed zeros, variant={variant}")
+        ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant)
+        mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, variant=variant)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev_bf16(ro), ref[0]) and np.array_equal(from_dev_bf16(out), ref[1])
+        assert np.array_equal(q.cpu().numpy(), ref[2]), "E4M3 codes differ (signed zeros included)"
+        assert np.array_equal(sc.cpu().numpy(), ref[3])
+        assert np.array_equal(from_dev_bf16(mout), ref_mx[1])
+        assert np.array_equal(mq.cpu().numpy(), ref_mx[2]), "E2M1 codes differ (signed zeros included)"
+        assert np.array_equal(msc.cpu().numpy(), ref_mx[3])
+
+
 # ------------------------------------------------------------------ graph capture
 def test_graph_capture_replays_match_eager(dev):
     """The calls allocate nothing and never synchronise, so a serving loop can capture them in a
@@ -378,7 +426,7 @@ def test_graph_capture_replays_match_eager(dev):
     torch.cuda.synchronize()
     # the eager results themselves against the oracle
     ra, rb = ua.oracle_rows(np.arange(ua.T), False), ub.oracle_rows(np.arange(ub.T), True)
-    rows_c = _sample_rows(uc.T, 24, seed=72)
+    rows_c = np.arange(uc.T)
     rc = uc.oracle_rows(rows_c, False)
     for (ro, out), r, rows in ((ea, ra, slice(None)), (eb[:2], rb, slice(None)), (ec, rc, rows_c)):
         ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro)[rows], r[0]),
@@ -468,15 +516,16 @@ def test_quant_alone_shapes(dev, H):
 
 
 # ------------------------------------------------------------------ MXFP4 output
-def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label=""):
+def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label="", ref=None):
     say(f"[gpu] mxfp4 {label} R={u.R} T={u.T} H={u.H} variant={variant} emit={emit_out}")
     ro, out, q, sc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, emit_out=emit_out, variant=VARIANTS[variant])
     torch.cuda.synchronize()
     rows = np.arange(u.T) if rows is None else np.asarray(rows)
     d = u.d
-    ref = oracle.reduce_add_rmsnorm_mxfp4(d["partials"][:, rows, :],
-                                          None if u.res is None else d["residual"][rows], d["gamma"], EPS,
-                                          emit_out, nthreads=8)
+    if ref is None:
+        ref = oracle.reduce_add_rmsnorm_mxfp4(d["partials"][:, rows, :],
+                                              None if u.res is None else d["residual"][rows], d["gamma"], EPS,
+                                              emit_out, nthreads=ORACLE_THREADS)
     ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro)[rows], ref[0]),
                                None if out is None else compare_bf16("out", from_dev_bf16(out)[rows], ref[1]), None)
     assert ok, f"{label}: {why}"
@@ -494,9 +543,10 @@ def test_mxfp4_configs(dev, name, variant):
     assert rep["n_code_diff"] == 0 and rep["n_scale_diff"] == 0  # bit-exact in practice
 
 
-@pytest.mark.parametrize("variant", ["latency", "bandwidth"])
-def test_mxfp4_prefill_sampled(prefill, variant):
-    run_mxfp4(prefill, variant, rows=_sample_rows(prefill.T), label="prefill")
+@pytest.mark.parametrize("variant", ["auto", "latency", "bandwidth"])
+def test_mxfp4_prefill_all_rows(prefill, variant):
+    rep = run_mxfp4(prefill, variant, label="prefill, every row", ref=_prefill_ref(prefill, "mxfp4"))
+    say(f"[gpu]   {rep}")
 
 
 @pytest.mark.parametrize("H", [32, 96, 160, 1024, 8224, 16384, 32768])
@@ -643,6 +693,24 @@ def test_binding_stream_handle(dev):
     with torch.cuda.stream(s):
         assert F._stream(dev, None) == torch.cuda.current_stream(dev).cuda_stream == s.cuda_stream
     assert F._stream(dev, s) == s.cuda_stream
+
+
+def test_explicit_stream_outputs(dev):
+    """A call given stream= (not the current stream) launches there with outputs the wrapper
+    allocates and marks as used on that stream; after that stream finishes they hold the
+    oracle's results."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=12, T=40)
+    u = Uploaded(d, dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    say("[gpu] explicit stream, wrapper-allocated outputs")
+    ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, stream=s)
+    s.synchronize()
+    ref = u.oracle_rows(np.arange(u.T), True)
+    ok, why = within_tolerance(compare_bf16("ro", from_dev_bf16(ro), ref[0]),
+                               compare_bf16("out", from_dev_bf16(out), ref[1]),
+                               compare_fp8(q.cpu().numpy(), ref[2], sc.cpu().numpy(), ref[3]))
+    assert ok, why
 
 
 def test_binding_rejects_bad_output_buffers(dev):

@@ -535,6 +535,39 @@ def check_mxfp4_fused_consistency():
     assert none is None and np.array_equal(q, q3) and np.array_equal(sc, sc3)
 
 
+# ============================================================================ threaded row split
+def check_threaded_rows_match_one_thread():
+    """The fused calls deal rows round-robin to threads. With 2, 3, 8 and 16 threads, on row
+    counts below, at and above the thread count and not multiples of it, every output must
+    equal the one-thread result bit for bit (outputs start poisoned, so a row no thread writes,
+    or one written twice with another row's values, shows). The one-thread path is what every
+    other pin holds to the definition."""
+    shapes = [(3, 1, 256), (2, 2, 128), (5, 3, 256), (4, 16, 384), (8, 17, 128), (2, 33, 256), (6, 50, 128)]
+    with oracle.threads(1):
+        for i, (R, T, H) in enumerate(shapes):
+            d = make_inputs(CONFIGS["decode_fp8"], seed=700 + i, R=R, T=T, H=H)
+            res = d["residual"] if i % 2 == 0 else None
+            ref = (oracle.reduce_add_rmsnorm(d["partials"], res, d["gamma"], EPS),
+                   oracle.reduce_add_rmsnorm_quant_group(d["partials"], res, d["gamma"], EPS),
+                   oracle.reduce_add_rmsnorm_quant_group(d["partials"], res, d["gamma"], EPS, emit_out=False),
+                   oracle.reduce_add_rmsnorm_mxfp4(d["partials"], res, d["gamma"], EPS),
+                   oracle.reduce_add_rmsnorm_mxfp4(d["partials"], res, d["gamma"], EPS, emit_out=False))
+            for n in (2, 3, 8, 16):
+                got = (oracle.reduce_add_rmsnorm(d["partials"], res, d["gamma"], EPS, nthreads=n),
+                       oracle.reduce_add_rmsnorm_quant_group(d["partials"], res, d["gamma"], EPS, nthreads=n),
+                       oracle.reduce_add_rmsnorm_quant_group(d["partials"], res, d["gamma"], EPS,
+                                                             emit_out=False, nthreads=n),
+                       oracle.reduce_add_rmsnorm_mxfp4(d["partials"], res, d["gamma"], EPS, nthreads=n),
+                       oracle.reduce_add_rmsnorm_mxfp4(d["partials"], res, d["gamma"], EPS, emit_out=False,
+                                                       nthreads=n))
+                for call, (a, b) in enumerate(zip(ref, got)):
+                    for k, (x, y) in enumerate(zip(a, b)):
+                        assert (x is None) == (y is None)
+                        if x is not None:
+                            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
+                                f"R={R} T={T} H={H} threads={n}: call {call} output {k} differs"
+
+
 ALL_CHECKS = [
     check_bf16_encoder_vs_torch_cast, check_bf16_golden_rounding_points, check_bf16_encoder_exact_on_doubles,
     check_e4m3_encoder_exhaustive_bf16, check_e4m3_encoder_exact_near_ties, check_e4m3_golden_codes,
@@ -547,12 +580,21 @@ ALL_CHECKS = [
     check_quant_zero_group_and_consistency, check_in_place_residual,
     check_reduce_alone, check_quant_alone,
     check_e2m1_encoder, check_mxfp4_blocks, check_mxfp4_fused_consistency,
+    check_threaded_rows_match_one_thread,
 ]
 
 
+# Every pin runs on the one-thread oracle and again with its rows dealt to 3 and to 7 threads
+# (outputs poisoned before each call): the GPU comparisons and the bench run the oracle
+# threaded, so the threaded row split is held to the same pins.
+PIN_THREADS = (1, 3, 7)
+
+
+@pytest.mark.parametrize("nthreads", PIN_THREADS, ids=lambda n: f"threads{n}")
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__[len("check_"):])
-def test_pin(check):
-    check()
+def test_pin(check, nthreads):
+    with oracle.threads(nthreads):
+        check()
 
 
 # ============================================================================ planted mistakes
@@ -630,6 +672,13 @@ MUTANTS = [
      "if (0)\n                    j->q[base + h] = 0x00u;\n                else\n"),
     ("mx_zero_block_unguarded", "} else if (amax == 0.0) {", "} else if (amax < 0.0) {"),
     ("mx_nan_block_unguarded", "if (isnan(a)) has_nan = 1;", "if (isnan(a)) has_nan = 0;"),
+    # the threaded row split: a wrong stride, a wrong first row, a thread never started
+    ("thread_row_stride", "for (int64_t t = j->tid; t < j->T; t += j->nthreads)",
+     "for (int64_t t = j->tid; t < j->T; t += j->nthreads + (j->tid == 0))"),
+    ("thread_first_row", "for (int64_t t = j->tid; t < j->T; t += j->nthreads)",
+     "for (int64_t t = j->tid + 1; t < j->T; t += j->nthreads)"),
+    ("thread_last_not_started", "for (int k = 1; k < n; ++k) {\n        if (pthread_create",
+     "for (int k = 1; k < n - 1; ++k) {\n        if (pthread_create"),
 ]
 
 
@@ -647,13 +696,17 @@ def test_planted_mistakes_are_caught(mutant, tmp_path):
     subprocess.run(["gcc", *oracle.CFLAGS, "-o", str(so), str(c), "-lm"], check=True)
     caught = []
     with oracle.using(str(so)):
-        for check in ALL_CHECKS:
-            try:
-                check()
-            except AssertionError:
-                caught.append(check.__name__)
-            except Exception:  # a crash or bad status also counts as caught
-                caught.append(check.__name__ + "!")
+        for n in PIN_THREADS:
+            for check in ALL_CHECKS:
+                try:
+                    with oracle.threads(n):
+                        check()
+                except AssertionError:
+                    caught.append(check.__name__)
+                except Exception:  # a crash or bad status also counts as caught
+                    caught.append(check.__name__ + "!")
+                if caught:
+                    break
             if caught:
                 break
     assert caught, f"planted mistake {name} passed every pin"

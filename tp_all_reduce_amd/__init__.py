@@ -116,6 +116,16 @@ def _stream(device, stream):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on_stream(stream, made):
+    """Outputs a wrapper allocates come from the caching allocator's pool of the current stream.
+    When the kernels are launched on another `stream`, mark them as used there, so that their
+    memory is not handed out again before that stream's work is done."""
+    if stream is not None:
+        for t in made:
+            if t is not None:
+                t.record_stream(stream)
+
+
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual_out=None,
                        out=None, variant: int = VARIANT_AUTO, stream=None):
     """Sum the R partials (list of bf16 [T,H] device tensors) in rank order in fp32, add the
@@ -123,8 +133,14 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float = 1e-6, *, residual
     residual_out may be the residual tensor itself (in place). Returns (residual_out, out)."""
     p0 = partials[0]
     dev = _device_of(p0)
-    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
-    out = torch.empty_like(p0) if out is None else out
+    made = []
+    if residual_out is None:
+        residual_out = torch.empty_like(p0)
+        made.append(residual_out)
+    if out is None:
+        out = torch.empty_like(p0)
+        made.append(out)
+    _on_stream(stream, made)
     st = _ext.fused(partials, residual, gamma, eps, residual_out, out, None, None, _PLAIN, 0, variant,
                     _stream(dev, stream))
     if st != OK:
@@ -142,15 +158,23 @@ def reduce_add_rmsnorm_quant_group(partials, residual, gamma, eps: float = 1e-6,
     p0 = partials[0]
     dev = _device_of(p0)
     T, H = p0.shape
-    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    made = []
+    if residual_out is None:
+        residual_out = torch.empty_like(p0)
+        made.append(residual_out)
     if emit_out and out is None:
         out = torch.empty_like(p0)
+        made.append(out)
     if not emit_out:
         out = None
-    q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        made.append(q)
     if scales is None:
         G = H // group_size if group_size > 0 else 0
         scales = torch.empty((G, T) if scales_col_major else (T, G), dtype=torch.float32, device=dev)
+        made.append(scales)
+    _on_stream(stream, made)
     st = _ext.fused(partials, residual, gamma, eps, residual_out, out, q, scales, _FP8, group_size,
                     variant | (SCALES_COL_MAJOR if scales_col_major else 0), _stream(dev, stream))
     if st != OK:
@@ -163,7 +187,9 @@ def reduce(partials, *, out=None, stream=None):
     sum of the partials. Returns out."""
     p0 = partials[0]
     dev = _device_of(p0)
-    out = torch.empty_like(p0) if out is None else out
+    if out is None:
+        out = torch.empty_like(p0)
+        _on_stream(stream, [out])
     st = _ext.reduce(partials, out, _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_reduce")
@@ -174,9 +200,14 @@ def quant_group(x, *, group_size: int = GROUP, q=None, scales=None, stream=None)
     """Per-group E4M3 quant alone of a bf16 [T,H] tensor. Returns (q uint8 [T,H], scales fp32 [T,H/128])."""
     dev = _device_of(x, "x")
     T, H = x.shape
-    q = torch.empty((T, H), dtype=torch.uint8, device=dev) if q is None else q
+    made = []
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        made.append(q)
     if scales is None:
         scales = torch.empty((T, H // group_size if group_size > 0 else 0), dtype=torch.float32, device=dev)
+        made.append(scales)
+    _on_stream(stream, made)
     st = _ext.quant(x, group_size, q, scales, _stream(dev, stream))
     if st != OK:
         raise FarnError(st, "farn_quant_group")
@@ -192,13 +223,22 @@ def reduce_add_rmsnorm_mxfp4(partials, residual, gamma, eps: float = 1e-6, *, em
     p0 = partials[0]
     dev = _device_of(p0)
     T, H = p0.shape
-    residual_out = torch.empty_like(p0) if residual_out is None else residual_out
+    made = []
+    if residual_out is None:
+        residual_out = torch.empty_like(p0)
+        made.append(residual_out)
     if emit_out and out is None:
         out = torch.empty_like(p0)
+        made.append(out)
     if not emit_out:
         out = None
-    q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev) if q is None else q
-    scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev) if scales is None else scales
+    if q is None:
+        q = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+        made.append(q)
+    if scales is None:
+        scales = torch.empty((T, H // MX_BLOCK), dtype=torch.uint8, device=dev)
+        made.append(scales)
+    _on_stream(stream, made)
     st = _ext.fused(partials, residual, gamma, eps, residual_out, out, q, scales, _MXFP4, 0, variant,
                     _stream(dev, stream))
     if st != OK:

@@ -169,18 +169,22 @@ __device__ __forceinline__ uint32_t pack_bf16_d(double lo, double hi) {
 // repeats the checks).
 
 // The binary32 quotient o / scale without a divide (inv = 1/scale): q0 = o * inv, the
-// remainder o - q0 * scale by one FMA, one correction q0 + r * inv by another. The result
-// can sit one fp32 unit off the correctly rounded quotient, but never where that changes
-// its E4M3 code: for every bf16 amax and every bf16 o the group can hold (tiny groups
-// rescaled by the caller) the codes agree (checked on the CPU over all 1.07e9 such pairs,
-// tests/test_encoder_models.py).
+// remainder by one FMA, one correction by another (Markstein's FMA correction of a
+// reciprocal product). The result can sit one fp32 unit off the correctly rounded
+// quotient, but never where that changes its E4M3 code: for every bf16 amax and every bf16
+// o the group can hold (tiny groups rescaled by the caller) the codes agree (checked on the
+// CPU over all 1.07e9 such pairs, tests/test_encoder_models.py).
+// The remainder is taken negated, nr = q0 * scale - o, and the correction is q0 - nr * inv:
+// the same value as q0 + (o - q0 * scale) * inv for every o (round to nearest is symmetric),
+// and a -0 input keeps its sign (-0 - (+0) = -0, where -0 + (+0) would give +0), so its code
+// is the -0 code 0x80, as the division gives.
 // scale_r is scale, or the largest finite float for an inf scale (so that the remainder of
-// a finite o is o rather than 0 * inf = NaN).
+// a finite o is -o rather than 0 * inf = NaN).
 __device__ __forceinline__ float fp32_quotient(float o, float scale_r, float inv) {
 #pragma clang fp contract(off)
     const float q0 = o * inv;
-    const float r = __builtin_fmaf(-q0, scale_r, o);
-    return __builtin_fmaf(r, inv, q0);
+    const float nr = __builtin_fmaf(q0, scale_r, -o);
+    return __builtin_fmaf(-nr, inv, q0);
 }
 
 // ---------------------------------------------------------------- cross-lane
