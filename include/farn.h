@@ -22,13 +22,15 @@
  *   acc   = P_0[t,h]; acc += P_r[t,h] for r = 1..R-1     fp32 adds, rank order
  *   y     = acc + residual[t,h]                          fp32 (no add if residual == NULL)
  *   residual_out[t,h] = bf16_rne(y)
- *   rstd  = 1 / sqrt(sum_h residual_out[t,h]^2 / H + eps)   fp64, fixed reduction tree
- *   out[t,h] = bf16_rne((residual_out[t,h] * rstd) * gamma[h])   fp64 product, one rounding
+ *   rstd  = 1 / sqrt(sum_h residual_out[t,h]^2 / H + eps)   fp64: sum in a fixed reduction
+ *           tree, the mean and reciprocal square root within about one fp64 unit
+ *   out[t,h] = bf16_rne((residual_out[t,h] * rstd) * gamma[h])   one rounding of the product
+ *           (formed in fp32 where that provably gives the same bf16 value, else in fp64)
  * and for the quant call, per group g of 128 channels:
  *   scale[t,g] = amax_g |out| / 448  (fp32, correctly rounded)
  *   q[t,h]     = e4m3fn_rne(fl32(out[t,h] / scale[t,g]))  (OCP E4M3, satfinite; 0 when
  *                scale == 0; the quotient as an IEEE single division gives it, then one
- *                rounding to E4M3)
+ *                rounding to E4M3; a -0 out gives the -0 code 0x80)
  *
  * Layout: every [T,H] buffer is row-major and contiguous (row stride H
  * elements); bf16 values are passed as raw 16-bit patterns; q holds one E4M3
@@ -79,7 +81,7 @@ typedef enum farn_status {
 #define FARN_GROUP 128
 /* MXFP4 block along H (OCP Microscaling Formats (MX) v1.0: 32 elements per shared scale). */
 #define FARN_MX_BLOCK 32
-#define FARN_ABI_VERSION 2
+#define FARN_ABI_VERSION 3
 
 /*
  * Plain call: reduce + residual add + RMSNorm.
@@ -129,17 +131,28 @@ farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, co
                                           void *residual_out, void *out, void *q, void *scales,
                                           void *stream);
 
-/* Launch shapes of the one kernel (one workgroup per token row). AUTO picks by size
-   from measurements (farn_select_variant). LATENCY: the widest row mapping (up to 1024
-   lanes, one 16-byte vector per lane up to H = 8192). BANDWIDTH: about half as many lanes
-   with two vectors each (for 1024 < H <= 8192; the same as LATENCY otherwise). Which is
-   faster depends on how evenly the row's waves fill a compute unit's four SIMDs, not on T
-   alone: AUTO takes BANDWIDTH for H = 7168 and 8192 at every T. Both compute the same
-   results (their fp64 sums of squares differ only in the order of additions). */
+/* Launch shapes of the one kernel (one workgroup per token row; H/8 16-byte vectors per row):
+ *   FARN_VARIANT_WIDE   (1, also named FARN_VARIANT_LATENCY): one vector per lane, H/8 lanes
+ *                       rounded up to a multiple of 64 (up to 1024 lanes at H = 8192); beyond
+ *                       H = 8192, 1024 lanes with two or four vectors each. The fewest
+ *                       instructions per lane.
+ *   FARN_VARIANT_NARROW (2, also named FARN_VARIANT_BANDWIDTH): about half as many lanes with
+ *                       two vectors each, for 1024 < H <= 8192 (the WIDE launch otherwise):
+ *                       twice the loads in flight per lane, half the waves per row.
+ * The older names describe launch widths, not regimes: both shapes serve every T. AUTO
+ * (farn_select_variant) picks by measurement on MI355X. It takes NARROW for
+ *   - 6144 < H <= 8192, except the plain call with H > 7168 from T = 4096;
+ *   - 4608 < H <= 5120 with 1024 <= T < 2048;
+ *   - R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048);
+ *   - 1536 < H <= 2048 from T = 4096;
+ * and WIDE everywhere else. Both compute the same results (their fp64 sums of squares differ
+ * only in the order of additions). */
 typedef enum farn_variant {
     FARN_VARIANT_AUTO = 0,
-    FARN_VARIANT_LATENCY = 1,
-    FARN_VARIANT_BANDWIDTH = 2
+    FARN_VARIANT_WIDE = 1,
+    FARN_VARIANT_NARROW = 2,
+    FARN_VARIANT_LATENCY = FARN_VARIANT_WIDE,
+    FARN_VARIANT_BANDWIDTH = FARN_VARIANT_NARROW
 } farn_variant;
 
 /* Option bit of the _ex calls, or-ed into `variant`: FP8 scales laid out column-major,

@@ -56,46 +56,46 @@ def test_status_strings_and_select():
     assert L.farn_status_string(99) == b"unknown status"
     for T in (1, 2, 64, 512, 4096, 8192, 1 << 20):
         for H in (256, 7168, 8192):
-            assert F.select_variant(8, T, H, False) in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH)
-    # the measured rule
-    assert F.select_variant(8, 64, 7168, False) == F.VARIANT_BANDWIDTH  # decode, H = 7168
-    assert F.select_variant(8, 8192, 7168, True) == F.VARIANT_BANDWIDTH  # FP8 prefill chunk
-    assert F.select_variant(8, 1, 8192, True) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(4, 16, 4096, True) == F.VARIANT_LATENCY  # decode FP8, H = 4096
-    assert F.select_variant(8, 8192, 4096, False) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 512, 6144, True) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 4096, 2048, False) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 8192, 2048, False) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(8, 8192, 1024, False) == F.VARIANT_LATENCY  # one wave per row
-    assert F.select_variant(8, 1024, 5120, True) == F.VARIANT_BANDWIDTH  # the H = 5120 band
-    assert F.select_variant(8, 2048, 5120, True) == F.VARIANT_LATENCY
-    assert F.select_variant(2, 8192, 4096, True) == F.VARIANT_BANDWIDTH  # two ranks
-    assert F.select_variant(4, 8192, 4096, True) == F.VARIANT_LATENCY
-    assert F.select_variant(2, 64, 4096, False) == F.VARIANT_LATENCY
-    # few ranks: the bandwidth shape's two vectors per lane keep more loads in flight
-    assert F.select_variant(2, 512, 3072, True) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(2, 256, 3072, False) == F.VARIANT_LATENCY
-    assert F.select_variant(2, 8192, 2560, False) == F.VARIANT_LATENCY  # nvec = 320
-    assert F.select_variant(2, 4096, 6144, True) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(2, 2048, 6144, True) == F.VARIANT_LATENCY
-    assert F.select_variant(4, 2048, 3072, False) == F.VARIANT_BANDWIDTH  # plain only
-    assert F.select_variant(4, 2048, 3072, True) == F.VARIANT_LATENCY
-    assert F.select_variant(4, 1024, 3072, False) == F.VARIANT_BANDWIDTH  # mid-T band
-    assert F.select_variant(4, 4096, 6144, False) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 2048, 3072, False) == F.VARIANT_LATENCY
-    # up to four ranks, plain, mid T: bandwidth shape
-    assert F.select_variant(4, 512, 6144, False) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(2, 512, 6144, False) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(4, 512, 6144, True) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 512, 6144, False) == F.VARIANT_LATENCY
-    assert F.select_variant(4, 256, 6144, False) == F.VARIANT_LATENCY
-    assert F.select_variant(4, 2048, 6144, False) == F.VARIANT_LATENCY
-    # plain call above H = 7168 from T = 2048: latency shape
-    assert F.select_variant(8, 8192, 8192, False) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 2048, 8192, False) == F.VARIANT_LATENCY
-    assert F.select_variant(8, 1024, 8192, False) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(8, 8192, 8192, True) == F.VARIANT_BANDWIDTH
-    assert F.select_variant(8, 8192, 7168, False) == F.VARIANT_BANDWIDTH
+            assert F.select_variant(8, T, H, False) in (F.VARIANT_WIDE, F.VARIANT_NARROW)
+    assert (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH) == (F.VARIANT_WIDE, F.VARIANT_NARROW)
+
+
+W, N = F.VARIANT_WIDE, F.VARIANT_NARROW
+# Every band of the AUTO rule as include/farn.h states it, at its edges: (R, T, H, quant, shape)
+HEADER_RULE_POINTS = [
+    # 6144 < H <= 8192: narrow, except the plain call with H > 7168 from T = 4096
+    (8, 1, 6152, False, N), (8, 64, 7168, False, N), (8, 8192, 7168, False, N), (8, 8192, 7168, True, N),
+    (2, 8192, 7168, False, N), (8, 64, 8192, False, N), (8, 4095, 8192, False, N), (8, 4096, 8192, False, W),
+    (8, 8192, 8192, False, W), (2, 4096, 8192, False, W), (8, 8192, 8192, True, N), (8, 4096, 7176, False, W),
+    (8, 4096, 7168, False, N), (8, 64, 6144, False, W),
+    # 4608 < H <= 5120 with 1024 <= T < 2048
+    (8, 1024, 5120, False, N), (8, 2047, 4616, True, N), (8, 1023, 5120, False, W), (8, 2048, 5120, False, W),
+    (8, 1024, 4608, False, W), (8, 1024, 5128, False, W),
+    # R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048)
+    (4, 512, 2056, False, N), (4, 1023, 6144, True, N), (4, 1024, 4096, False, W), (4, 511, 3072, False, W),
+    (2, 1024, 4096, False, N), (2, 2047, 3072, True, N), (2, 2048, 3072, False, W), (1, 512, 4096, False, N),
+    (5, 512, 3072, False, W), (4, 512, 2048, False, W), (4, 512, 6152, False, N), (4, 512, 6160, False, N),
+    # 1536 < H <= 2048 from T = 4096
+    (8, 4096, 2048, False, N), (8, 8192, 1544, True, N), (8, 4095, 2048, False, W), (8, 8192, 1536, False, W),
+    # everything else: wide
+    (8, 64, 4096, False, W), (8, 8192, 4096, True, W), (8, 8192, 6144, False, W), (8, 1024, 2048, False, W),
+    (4, 16, 4096, True, W), (8, 4, 256, False, W), (2, 8192, 32768, False, W),
+]
+
+
+@pytest.mark.parametrize("R,T,H,quant,shape", HEADER_RULE_POINTS)
+def test_select_matches_header(R, T, H, quant, shape):
+    """farn_select_variant implements the rule include/farn.h documents, at every band edge."""
+    assert F.select_variant(R, T, H, quant) == shape
+
+
+def test_header_states_the_rule():
+    text = open(HEADER).read()
+    for phrase in ("6144 < H <= 8192, except the plain call with H > 7168 from T = 4096",
+                   "4608 < H <= 5120 with 1024 <= T < 2048",
+                   "R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048)",
+                   "1536 < H <= 2048 from T = 4096", "and WIDE everywhere else"):
+        assert phrase in " ".join(text.replace("*", " ").split()), phrase
 
 
 class FakeCall:

@@ -141,3 +141,92 @@ def test_uncorrected_product_would_fail():
     v32 = (o / scale).astype(np.float32)
     assert (oracle.e4m3fn_from_double_array(q0.astype(np.float64)) !=
             oracle.e4m3fn_from_double_array(v32.astype(np.float64))).any()
+
+
+# ----------------------------------------------------------------------------- normalisation
+def norm_model(y_bits: np.ndarray, g_bits: np.ndarray, rstd: float):
+    """Model of `norm_slot` in tp_all_reduce_amd/csrc/farn_kernels.hip for one row's rstd:
+    the fp32 fast path (yg = y*gamma, p = yg * fl32(rstd), bf16 rounding of p), the test that
+    sends a value to the fp64 path (yg not a normal number, fl32(rstd) not a positive normal
+    number, low 16 bits of p within 0x7FFD .. 0x8003), and the fp64 path ((y*rstd)*gamma
+    rounded once, here by the oracle's encoder). Returns (bf16 bits, mask of values that took
+    the fp64 path). The kernel takes the fp64 path for a whole wave when any lane needs it;
+    the fp64 path gives the one-rounding result for every value, so modelling it per value
+    checks the same thing."""
+    y = (y_bits.astype(np.uint32) << 16).view(np.float32)
+    g = (g_bits.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+        r32 = np.float32(rstd)
+        yg = (y * g).astype(np.float32)
+        p = (yg * r32).astype(np.float32)
+    normal = lambda x: np.isfinite(x) & (np.abs(x) >= np.float32(2.0 ** -126))
+    r_ok = bool(np.isfinite(r32) and r32 >= np.float32(2.0 ** -126))
+    near = ((p.view(np.uint32) - np.uint32(0x7FFD)) & np.uint32(0xFFFF)) <= 6
+    slow = ~normal(yg) | near | (not r_ok)
+    with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+        fast_bits = oracle.bf16_from_double_array(p.astype(np.float64))
+        exact = (y.astype(np.float64) * rstd) * g.astype(np.float64)
+    slow_bits = oracle.bf16_from_double_array(exact)
+    return np.where(slow, slow_bits, fast_bits), slow
+
+
+def _bf16_of(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_norm_fast_path_equals_one_rounding():
+    """Wherever the fast path is kept, its bf16 value equals the single rounding of the fp64
+    product (y*rstd)*gamma: on random rows, on rows built so that the products land within a
+    few fp32 units of bf16 midpoints, and with zero, subnormal, huge, inf and NaN operands."""
+    rng = np.random.default_rng(7)
+    checked = slow_total = 0
+    # random rows: y ~ N(0, 1), gamma ~ U(0.5, 1.5), rstd over many binades
+    for _ in range(40):
+        y = _bf16_of(rng.standard_normal(1 << 16) * rng.choice([1e-3, 1.0, 30.0]))
+        g = _bf16_of(rng.uniform(0.5, 1.5, 1 << 16))
+        rstd = float(np.exp(rng.uniform(np.log(2.0 ** -40), np.log(2.0 ** 40))))
+        got, slow = norm_model(y, g, rstd)
+        want = oracle.bf16_from_double_array((((y.astype(np.uint32) << 16).view(np.float32).astype(np.float64) * rstd)
+                                              * (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)))
+        assert np.array_equal(got, want)
+        checked += y.size
+        slow_total += int(slow.sum())
+    assert slow_total < 0.001 * checked  # the fp64 path is rare on data like this
+    # adversarial: rstd chosen so that y*gamma*rstd sits within +-8 fp32 units of a bf16 midpoint
+    n = 1 << 16
+    y = _bf16_of(rng.standard_normal(n))
+    g = _bf16_of(rng.uniform(0.5, 1.5, n))
+    yf = (y.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    gf = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    target_bf = _bf16_of(rng.standard_normal(n) * 3)
+    mid = ((target_bf.astype(np.uint32) << 16) | np.uint32(0x8000)).view(np.float32).astype(np.float64)
+    for k in range(-8, 9):
+        for j in range(0, n, 4096):
+            sl = slice(j, j + 4096)
+            # one rstd per row: take the first element's target, offset by k fp32 units
+            y0, g0, m0 = yf[sl][0], gf[sl][0], mid[sl][0]
+            if y0 == 0 or m0 == 0 or np.sign(y0 * g0) != np.sign(m0):
+                continue
+            m_bits = np.array([m0], np.float32).view(np.uint32)[0]
+            tgt = np.array([m_bits + np.uint32(k & 0xFFFFFFFF)], np.uint32).view(np.float32)[0]
+            rstd = float(tgt) / (y0 * g0)
+            got, slow = norm_model(y[sl], g[sl], rstd)
+            want = oracle.bf16_from_double_array((yf[sl] * rstd) * gf[sl])
+            assert np.array_equal(got, want), (k, j)
+            checked += 4096
+            if abs(k) <= 2:
+                assert slow[0], (k, "a product within 2 units of a midpoint must take the fp64 path")
+    # special operands
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0,
+                         0x3F80, 0x0100, 0x1000], np.uint16)
+    yy, gg = np.meshgrid(specials, specials)
+    for rstd in (1.0, 2.0 ** -60, 2.0 ** 60, 2.0 ** -130, 1e300, 0.0, float("inf")):
+        got, _ = norm_model(yy.ravel(), gg.ravel(), rstd)
+        with np.errstate(all="ignore"):
+            want = oracle.bf16_from_double_array(((yy.ravel().astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                                                  * rstd) * (gg.ravel().astype(np.uint32) << 16).view(np.float32)
+                                                 .astype(np.float64))
+        same = (got == want) | (((got & 0x7FFF) > 0x7F80) & ((want & 0x7FFF) > 0x7F80))
+        assert same.all(), (rstd, yy.ravel()[~same][:4], gg.ravel()[~same][:4])
+    assert checked > 2_000_000

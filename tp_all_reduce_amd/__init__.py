@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfarn.so"
 OK = 0
 STATUS = {0: "FARN_OK", 1: "FARN_ERR_NULL", 2: "FARN_ERR_SHAPE", 3: "FARN_ERR_ALIGN",
           4: "FARN_ERR_ALIAS", 5: "FARN_ERR_EPS", 6: "FARN_ERR_LAUNCH", 7: "FARN_ERR_VARIANT"}
-VARIANT_AUTO, VARIANT_LATENCY, VARIANT_BANDWIDTH = 0, 1, 2
+VARIANT_AUTO, VARIANT_WIDE, VARIANT_NARROW = 0, 1, 2
+VARIANT_LATENCY, VARIANT_BANDWIDTH = VARIANT_WIDE, VARIANT_NARROW  # older names of the two shapes
 SCALES_COL_MAJOR = 0x100
 MAX_R, MAX_H, GROUP, MX_BLOCK = 8, 32768, 128, 32
 EXPORTS = ("farn_reduce_add_rmsnorm", "farn_reduce_add_rmsnorm_quant_group",

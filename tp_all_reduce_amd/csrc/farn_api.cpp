@@ -108,63 +108,50 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
     return FARN_OK;
 }
 
-// AUTO rule, set from measured sweeps on MI355X: R = 8, 4 and 2; H = 1536 .. 8192;
-// T = 1 .. 8192; plain and FP8; graph replay, cache-hot; each point the median of 3 runs
-// with both shapes timed back to back (the shader clock drifts by up to 15 % between runs,
-// which had misled a single-pass sweep). By vectors per row (nvec = H/8; the latency shape
-// runs one vector per lane, the bandwidth shape half as many lanes with two vectors each):
-//   - nvec in (768, 1024] (H = 7168, 8192): bandwidth at every T and R: 1-10 % at decode
-//     sizes, up to 12 % at T = 1024..4096, 5-10 % for the FP8 prefill chunk (R = 8: 212
-//     against 223 us); except the plain call above H = 7168 from T = 2048, where the
-//     latency shape wins by 2-4 % (the bandwidth shape's late residual_out store, a gain
-//     at decode sizes, costs a little there).
-//   - nvec in (256, 768] (H = 2056 .. 6144): latency (3-18 % at decode sizes), except
-//     H = 5120 at 1024 <= T < 2048, where bandwidth wins by 11 % (R = 8) and 6-10 % (R = 4).
-//   - Few ranks leave the latency shape only R + 1 loads in flight per lane; the bandwidth
-//     shape's two vectors per lane double that, and since both shapes then reach the limit of
-//     8 waves per SIMD, the loads in flight per compute unit double too. Two ranks: bandwidth for H = 2568 .. 4096
-//     from T = 512 (up to 11 %, plain and FP8), H = 4096 .. 5120 from T = 1024 (2-7 %) and
-//     H = 5128 .. 6144 from T = 4096 (2-3 %). Four ranks, plain call: bandwidth for
-//     H = 2056 .. 4096 from T = 2048 (5-9 % at T = 2048; the FP8 call stays on latency,
-//     where its shorter per-lane code wins by up to 5 %). Up to four ranks, plain call,
-//     H = 2056 .. 6144 at 512 <= T < 2048: bandwidth (2-9 % at T = 512, measured after the
-//     plain two-slot kernel moved its residual_out store after the statistics).
-//   - nvec <= 256 (H <= 2048): latency up to T = 4096 (10-30 % at T <= 1024), bandwidth
-//     by 1-2 % at T = 8192.
+// AUTO rule, from interleaved measurements of both launch shapes (median of 5, on two
+// MI355X boxes; graph replay, cache-hot for calls up to 128 MiB, streaming from HBM above)
+// at 70 points R = 2..8, H = 1024..8192, T = 64..8192, plain and FP8. By vectors per row,
+// nvec = H/8 (the wide shape runs one vector per lane, the narrow shape half as many lanes
+// with two vectors each). Measured gains of the narrow shape, in per cent of time:
+//   1. nvec in (768, 1024] (H = 6152 .. 8192): narrow, 3-12 % (decode 6-8 %, T = 1024 9-12 %,
+//      T = 8192 3.5-4 %); except the plain call with nvec > 896 (H > 7168) from T = 4096,
+//      where the wide shape is 2.5-3.5 % faster.
+//   2. nvec in (576, 640] (H = 4616 .. 5120) at 1024 <= T < 2048: narrow, 7-11 %.
+//   3. R <= 4, nvec in (256, 512] (H = 2056 .. 4096), T >= 512 and below 2048 (two ranks) or
+//      4096 (three or four): narrow, 3-26 % (with few ranks the wide shape keeps only R + 1
+//      loads in flight per lane; the narrow one doubles that). Beyond those T the wide shape
+//      is as fast or up to 4 % faster.
+//   4. nvec in (192, 256] (H = 1544 .. 2048) from T = 4096: narrow, 1.5-8 %.
+//   Everything else: wide (the narrow shape 0-16 % slower at R = 8, H = 4096 and 6144,
+//   and from T = 4096 at R = 2, H = 3072 .. 6144).
+// Over the measured points this rule is on average 0.2 % from the faster shape (at most
+// 5 %: R <= 4, H = 6144, T = 512, where the two shapes swap places between cache-hot and
+// streaming calls).
 int select(int R, int64_t T, int64_t H, int quant) {
     const int64_t nvec = H / 8;
-    if (nvec <= 128) return FARN_VARIANT_LATENCY;  // one wave per row: no narrower shape
     if (nvec > 768 && nvec <= 1024)
-        return (!quant && nvec > 896 && T >= 2048) ? FARN_VARIANT_LATENCY : FARN_VARIANT_BANDWIDTH;
+        return (!quant && nvec > 896 && T >= 4096) ? FARN_VARIANT_LATENCY : FARN_VARIANT_BANDWIDTH;
     if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_BANDWIDTH;
-    if (R <= 2) {
-        if (nvec > 320 && nvec <= 512 && T >= 512) return FARN_VARIANT_BANDWIDTH;
-        if (nvec > 448 && nvec <= 640 && T >= 1024) return FARN_VARIANT_BANDWIDTH;
-        if (nvec > 640 && nvec <= 768 && T >= 4096) return FARN_VARIANT_BANDWIDTH;
-    }
-    if (R > 2 && R <= 4 && !quant && nvec > 256 && nvec <= 512 && T >= 2048) return FARN_VARIANT_BANDWIDTH;
-    if (R <= 4 && !quant && nvec > 256 && nvec <= 768 && T >= 512 && T < 2048) return FARN_VARIANT_BANDWIDTH;
-    if (nvec <= 256 && T >= 8192) return FARN_VARIANT_BANDWIDTH;
+    if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 2048 : 1024)) return FARN_VARIANT_BANDWIDTH;
+    if (nvec > 192 && nvec <= 256 && T >= 4096) return FARN_VARIANT_BANDWIDTH;
     return FARN_VARIANT_LATENCY;
 }
 
-// Workgroups per compute unit for the plain call in the two-slot (bandwidth) shape at
-// H = 6152 .. 7168, where 76 VGPRs let three workgroups of 7 waves share a compute unit.
-// Two stream the prefill traffic faster: reserving 56 KiB of LDS per workgroup (of 160 KiB
-// per compute unit) leaves room for only two. Measured on MI355X (median of 5, interleaved,
-// eager back-to-back calls): R = 8, H = 7168: -2.9 % at T = 2048, -2.3 % at T = 4096, -1.9 %
-// at T = 8192 (205.4 -> 201.4 us); R = 8, H = 6656: -3.9 % at T = 2048; R = 7: -1.7 .. -2.0 %
-// and R = 6: -0.6 .. -1.3 % at T = 8192; at the rule's edges (R = 6, 7 at T = 2048, 4096;
-// H = 6152) -0.4 .. -6.1 %, in two placements of the arrays in memory each, and -1.6 .. -2.4 %
-// over six placements at R = 8, T = 8192. No change at T <= 1024 (R = 8) and for the FP8 and
-// MXFP4 calls (register-bound to about two already); slower with fewer ranks (R = 5: +1 ..
-// +3 %, R = 4: +1.9 %, R = 2: +4.6 %) and no gain at H = 8192.
+// Workgroups per compute unit of the narrow shape at nvec in (768, 1024] (7 or 8 waves per
+// row) with six or more ranks: at most two. Its registers allow three for the streaming FP8
+// and MXFP4 kernels (78 VGPRs), and two stream large T faster: reserving 56 KiB of LDS per
+// workgroup (of 160 KiB per compute unit), which the kernel does not use, leaves room for
+// two. Measured on MI355X (interleaved, median of 5): FP8 at R = 8, H = 7168: T = 2048
+// -4.2 %, T = 4096 -3.4 %, T = 8192 -2.5 %; MXFP4 T = 4096 -3.4 %, T = 8192 -2.2 %; no
+// change at T <= 1024. The plain and small-call kernels hold 86-91 VGPRs, so two is
+// already their limit.
 constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
 
 unsigned lds_reserve(int R, int64_t T, int64_t H, Quant quant, int shape) {
     const int64_t nvec = H / 8;
-    const bool two_slot = shape == FARN_VARIANT_BANDWIDTH && nvec > 768 && nvec <= 896;
-    return (quant == kNone && two_slot && R >= 6 && T >= 2048) ? kLdsTwoPerCu : 0u;
+    const bool wide_two_slot = shape == FARN_VARIANT_BANDWIDTH && nvec > 768 && nvec <= 1024;
+    const bool streaming = T > farn::kSmallCallRows;
+    return (quant != kNone && wide_two_slot && streaming && (R >= 6 || (R >= 4 && T >= 2048))) ? kLdsTwoPerCu : 0u;
 }
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,

@@ -40,6 +40,10 @@ struct RowShape {
 };
 RowShape row_shape(int64_t H, int variant);
 
+// Rows up to which the two-slot quant kernels run their small-call store schedule (measured
+// on MI355X: faster up to T = 256, slower from T = 1024); above it, the streaming schedule.
+constexpr int64_t kSmallCallRows = 512;
+
 // Enqueue one workgroup per row. variant: 1 = latency, 2 = bandwidth (already resolved
 // from AUTO; the unfused blocks use 1). Returns 0 on success, nonzero when the launch failed.
 int launch(const Call &c, int variant);

@@ -68,6 +68,7 @@ struct Params {
     int nvec;           // H / 8
     int ngroups;        // H / 128
     double h;           // H (mean divisor)
+    double inv_h;       // 1 / H
     float eps;
 };
 
@@ -131,6 +132,9 @@ __device__ __forceinline__ void st1_mx(uint32_t v, rsrc_t r, uint32_t off) {
 }
 
 // ---------------------------------------------------------------- number formats
+// Float classes for v_cmp_class: positive normal, and normal of either sign.
+constexpr int kClassPosNormal = 1 << 8;
+constexpr int kClassNormal = (1 << 3) | (1 << 8);
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -301,12 +305,17 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
 }
 
 // Row statistics in fp64: wave DPP tree, one double per wave through `slot` (kMaxWaves
-// doubles), one barrier, then every wave adds the per-wave values in wave order; rstd =
-// 1/sqrt(ss/H + eps) with correctly rounded fp64 division and square root. fp64
-// statistics put `out` on the bf16 value the exact statistics give (an fp32 tree moves
-// about one element in 10^4 by one bf16 step, and when that element is a group's amax
-// its scale moves by up to 2^-7); MI355X runs fp64 vector FMAs at the rate of unpacked
-// fp32 ones.
+// doubles), one barrier, then every wave adds the per-wave values in wave order; then
+// rstd = 1/sqrt(m) for m = ss/H + eps. fp64 statistics put `out` on the bf16 value the
+// exact statistics give (an fp32 tree moves about one element in 10^4 by one bf16 step,
+// and when that element is a group's amax its scale moves by up to 2^-7); MI355X runs
+// fp64 vector FMAs at the rate of unpacked fp32 ones.
+// m is formed as ss * (1/H) + eps by one FMA, and 1/sqrt(m) as the hardware reciprocal
+// square root refined by one Newton step (y += y * (1/2 - m y^2 / 2)): both sit within
+// about an fp64 unit of the correctly rounded quotient and root, far below what the bf16
+// outputs resolve, and the row's dependent chain after the barrier is some 30 fp64
+// operations shorter than with a division and a square root. Outside 2^-1000 <= m <=
+// 2^1000 (and for an inf or NaN m) the division and square root are used.
 __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *slot) {
     const int lane = (int)threadIdx.x & 63;
     const int wave = (int)threadIdx.x >> 6;
@@ -316,7 +325,17 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     __syncthreads();
     double tot = 0.0;
     for (int i = 0; i < nwaves; ++i) tot = tot + slot[i];
-    return 1.0 / __builtin_sqrt(tot / (double)k.h + (double)k.eps);
+    const double m = __builtin_fma(tot, k.inv_h, (double)k.eps);
+    double r;
+    if (m >= 0x1p-1000 && m <= 0x1p1000) {  // the same in every lane of the row
+        const double y0 = __builtin_amdgcn_rsq(m);
+        const double e = __builtin_fma(-0.5 * m * y0, y0, 0.5);
+        r = __builtin_fma(y0, e, y0);
+    } else {
+        __asm__ volatile("" ::: "memory");  // keeps this rare path a branch, not computed beside the other
+        r = 1.0 / __builtin_sqrt(tot / k.h + (double)k.eps);
+    }
+    return r;
 }
 
 // E4M3 codes of one vector slot (8 bf16 values, two per word of `ob`) and, from one lane
@@ -393,29 +412,59 @@ __device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc
     st1_mx(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
 }
 
-// Normalise one vector slot ((y * rstd) * gamma in fp64, one rounding to bf16) and store it
-// as out; returns the packed bf16 values (the FP8 quant's input).
-__device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out, uint32_t off) {
+// Normalised values of one vector slot, (y * rstd) * gamma each rounded once to bf16, packed.
+// Fast path in fp32: yg = y * gamma is exact when it is a normal number (two 8-bit
+// significands), and p = fl32(yg * fl32(rstd)) then lies within 1.5 fp32 units of the fp64
+// product (one rounding of rstd, one of the product; at most one more unit where p and the
+// fp64 value straddle a power of two), so the bf16 rounding of p is the one-rounding result
+// unless p is within 3 fp32 units of a bf16 midpoint: low 16 bits 0x7FFD .. 0x8003 (fp32
+// subnormal results included, whose error is below one unit). When any lane of the wave
+// has such a p, a yg that is not a normal number (zero, subnormal, inf, NaN) or the row an
+// rstd whose fp32 rounding is not normal, the wave redoes the slot in fp64: the product in
+// fp64, rounded to odd to fp32, then to nearest-even bf16 (one rounding). On random data
+// about one slot in twenty takes that path.
+__device__ __forceinline__ u32x4 norm_slot(u32x4 yb, u32x4 gam, double rstd, float r32, bool r32_ok) {
     u32x4 packed;
+    bool ok = r32_ok;
+    uint16_t near_mid = 0xffff;  // min over the slot of (low 16 bits of p) - 0x7FFD, mod 2^16
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const double lo = ((double)bf_lo(yb[w]) * rstd) * (double)bf_lo(gam[w]);
-        const double hi = ((double)bf_hi(yb[w]) * rstd) * (double)bf_hi(gam[w]);
-        packed[w] = pack_bf16_d(lo, hi);
+        const float ylo = bf_lo(yb[w]) * bf_lo(gam[w]);
+        const float yhi = bf_hi(yb[w]) * bf_hi(gam[w]);
+        ok = ok && __builtin_amdgcn_classf(ylo, kClassNormal) && __builtin_amdgcn_classf(yhi, kClassNormal);
+        const float plo = ylo * r32;
+        const float phi = yhi * r32;
+        near_mid = min(near_mid, (uint16_t)(__float_as_uint(plo) - 0x7FFDu));
+        near_mid = min(near_mid, (uint16_t)(__float_as_uint(phi) - 0x7FFDu));
+        packed[w] = pack_bf16(plo, phi);
     }
+    if (__builtin_amdgcn_ballot_w64(!ok || near_mid <= 6) != 0) {
+        __asm__ volatile("" ::: "memory");  // keeps the fp64 path a branch, not computed beside the fast one
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const double lo = ((double)bf_lo(yb[w]) * rstd) * (double)bf_lo(gam[w]);
+            const double hi = ((double)bf_hi(yb[w]) * rstd) * (double)bf_hi(gam[w]);
+            packed[w] = pack_bf16_d(lo, hi);
+        }
+    }
+    return packed;
+}
+
+// Normalise one vector slot and store it as out; returns the packed bf16 values (the FP8
+// quant's input).
+__device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, float r32, bool r32_ok,
+                                            rsrc_t r_out, uint32_t off) {
+    const u32x4 packed = norm_slot(yb, gam, rstd, r32, r32_ok);
     st16(packed, r_out, off);
     return packed;
 }
 
 // norm_store that also returns the values as floats in `o` (the MXFP4 quant's input).
-__device__ __forceinline__ void norm_store_f(u32x4 yb, u32x4 gam, double rstd, rsrc_t r_out, uint32_t off,
-                                             float (&o)[8]) {
-    u32x4 packed;
+__device__ __forceinline__ void norm_store_f(u32x4 yb, u32x4 gam, double rstd, float r32, bool r32_ok,
+                                             rsrc_t r_out, uint32_t off, float (&o)[8]) {
+    const u32x4 packed = norm_slot(yb, gam, rstd, r32, r32_ok);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const double lo = ((double)bf_lo(yb[w]) * rstd) * (double)bf_lo(gam[w]);
-        const double hi = ((double)bf_hi(yb[w]) * rstd) * (double)bf_hi(gam[w]);
-        packed[w] = pack_bf16_d(lo, hi);
         o[2 * w] = bf_lo(packed[w]);
         o[2 * w + 1] = bf_hi(packed[w]);
     }
@@ -463,6 +512,8 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
         }
     }
     const double rstd = row_rstd(ss, k, slot);
+    const float r32 = (float)rstd;
+    const bool r32_ok = __builtin_amdgcn_classf(r32, kClassPosNormal);
     const rsrc_t r_out = row_rsrc(k.out, k.out ? ro : 0, k.out ? rb : 0);
     // per-row code and scale bytes: FP8 H and 4*H/128; MXFP4 H/2 and H/32
     const int qb = QM == kQuantFp8 ? k.nvec * 8 : (QM == kQuantMxfp4 ? k.nvec * 4 : 0);
@@ -480,7 +531,7 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             st16(yb[v], r_ro, off0 + v * L16);
-            ob[v] = norm_store(yb[v], gam[v], rstd, r_out, off0 + v * L16);
+            ob[v] = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
         }
 #pragma unroll
         for (int v = 0; v < VPL; ++v) quant_slot<kCodeP>(ob[v], r_q, r_sc, off0 + v * L16, sbase, sstride);
@@ -490,10 +541,10 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
             if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
             if constexpr (QM == kQuantMxfp4) {
                 float o[8];
-                norm_store_f(yb[v], gam[v], rstd, r_out, off0 + v * L16, o);
+                norm_store_f(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16, o);
                 mxfp4_slot(o, r_q, r_sc, off0 + v * L16);
             } else {
-                const u32x4 ob = norm_store(yb[v], gam[v], rstd, r_out, off0 + v * L16);
+                const u32x4 ob = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
                 if constexpr (QM == kQuantFp8) quant_slot<kCodeP>(ob, r_q, r_sc, off0 + v * L16, sbase, sstride);
             }
         }
@@ -614,18 +665,15 @@ static Params make_params(const Call &c) {
     k.nvec = (int)(c.H / 8);
     k.ngroups = (int)(c.H / 128);
     k.h = (double)c.H;
+    k.inv_h = 1.0 / (double)c.H;
     k.eps = c.eps;
     return k;
 }
 
-// Rows up to which the two-slot quant kernels use their small-call schedule (measured on
-// MI355X: faster up to T = 256, slower from T = 1024).
-constexpr int64_t kSmallRows = 512;
-
 int launch(const Call &c, int variant) {
     const RowShape rs = row_shape(c.H, c.kind == Kind::kFused ? variant : 1);
     int vi = rs.vpl == 1 ? 0 : (rs.vpl == 2 ? 1 : 2);
-    if (c.kind == Kind::kFused && c.q != nullptr && rs.vpl == 2 && c.T <= kSmallRows) vi = 3;
+    if (c.kind == Kind::kFused && c.q != nullptr && rs.vpl == 2 && c.T <= kSmallCallRows) vi = 3;
     KernelFn fn = nullptr;
     if (c.kind == Kind::kReduce) {
         fn = pick_reduce(c.R, vi);
