@@ -14,7 +14,7 @@ namespace farn {
 RowShape row_shape(int64_t H, int variant) {
     const int64_t nvec = H / 8;
     RowShape s;
-    if (variant == FARN_VARIANT_BANDWIDTH && nvec > 128 && nvec <= 1024) {
+    if (variant == FARN_VARIANT_NARROW && nvec > 128 && nvec <= 1024) {
         s.lanes = (int)((((nvec + 1) / 2) + 63) / 64 * 64);  // about NV/2 lanes, two vectors each
         s.vpl = 2;
     } else if (nvec <= 1024) {
@@ -110,48 +110,49 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 
 // AUTO rule, from interleaved measurements of both launch shapes (median of 5, on two
 // MI355X boxes; graph replay, cache-hot for calls up to 128 MiB, streaming from HBM above)
-// at 70 points R = 2..8, H = 1024..8192, T = 64..8192, plain and FP8. By vectors per row,
+// at 75 points R = 2..8, H = 1024..8192, T = 64..8192, plain and FP8. By vectors per row,
 // nvec = H/8 (the wide shape runs one vector per lane, the narrow shape half as many lanes
-// with two vectors each). Measured gains of the narrow shape, in per cent of time:
-//   1. nvec in (768, 1024] (H = 6152 .. 8192): narrow, 3-12 % (decode 6-8 %, T = 1024 9-12 %,
-//      T = 8192 3.5-4 %); except the plain call with nvec > 896 (H > 7168) from T = 4096,
-//      where the wide shape is 2.5-3.5 % faster.
-//   2. nvec in (576, 640] (H = 4616 .. 5120) at 1024 <= T < 2048: narrow, 7-11 %.
-//   3. R <= 4, nvec in (256, 512] (H = 2056 .. 4096), T >= 512 and below 2048 (two ranks) or
-//      4096 (three or four): narrow, 3-26 % (with few ranks the wide shape keeps only R + 1
-//      loads in flight per lane; the narrow one doubles that). Beyond those T the wide shape
-//      is as fast or up to 4 % faster.
-//   4. nvec in (192, 256] (H = 1544 .. 2048) from T = 4096: narrow, 1.5-8 %.
-//   Everything else: wide (the narrow shape 0-16 % slower at R = 8, H = 4096 and 6144,
-//   and from T = 4096 at R = 2, H = 3072 .. 6144).
-// Over the measured points this rule is on average 0.2 % from the faster shape (at most
-// 5 %: R <= 4, H = 6144, T = 512, where the two shapes swap places between cache-hot and
-// streaming calls).
+// with two vectors each). Time of the narrow shape against the wide one:
+//   1. nvec in (768, 1024] (H = 6152 .. 8192): narrow, -3 .. -9.5 % (decode -5 .. -9 %,
+//      T = 1024 -9 %, T = 8192 -3.3 .. -4.5 %; ties at H = 8192, T = 2048); except the plain
+//      call with nvec > 896 (H > 7168) from T = 4096, where the wide shape is 0.5-2 % faster
+//      at R = 8.
+//   2. nvec in (576, 640] (H = 4616 .. 5120) at 1024 <= T < 2048: narrow, -9 .. -12 % at
+//      R = 8, -2 .. -3 % at R = 2.
+//   3. R <= 4, nvec in (256, 768] (H = 2056 .. 6144) at 512 <= T < 1024 (two ranks: T < 2048):
+//      narrow, up to -22 % (FP8 at T = 512). With few ranks the wide shape keeps only R + 1
+//      loads in flight per lane; the narrow one doubles that. From T = 1024 (four ranks) or
+//      2048 (two) the wide shape is as fast or up to 7 % faster.
+//   4. nvec in (192, 256] (H = 1544 .. 2048) from T = 4096: narrow, -1.5 .. -9 %.
+//   Everything else: wide (the narrow shape up to 7.7 % slower: R = 8, H = 4096 decode).
+// Over the measured points this rule is on average 0.17 % from the faster shape, at most
+// 2.8 % (R = 4, H = 3072, T = 2048, FP8, narrow faster).
 int select(int R, int64_t T, int64_t H, int quant) {
     const int64_t nvec = H / 8;
     if (nvec > 768 && nvec <= 1024)
-        return (!quant && nvec > 896 && T >= 4096) ? FARN_VARIANT_LATENCY : FARN_VARIANT_BANDWIDTH;
-    if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_BANDWIDTH;
-    if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 2048 : 1024)) return FARN_VARIANT_BANDWIDTH;
-    if (nvec > 192 && nvec <= 256 && T >= 4096) return FARN_VARIANT_BANDWIDTH;
-    return FARN_VARIANT_LATENCY;
+        return (!quant && nvec > 896 && T >= 4096) ? FARN_VARIANT_WIDE : FARN_VARIANT_NARROW;
+    if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_NARROW;
+    if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 2048 : 1024)) return FARN_VARIANT_NARROW;
+    if (nvec > 192 && nvec <= 256 && T >= 4096) return FARN_VARIANT_NARROW;
+    return FARN_VARIANT_WIDE;
 }
 
-// Workgroups per compute unit of the narrow shape at nvec in (768, 1024] (7 or 8 waves per
-// row) with six or more ranks: at most two. Its registers allow three for the streaming FP8
-// and MXFP4 kernels (78 VGPRs), and two stream large T faster: reserving 56 KiB of LDS per
-// workgroup (of 160 KiB per compute unit), which the kernel does not use, leaves room for
-// two. Measured on MI355X (interleaved, median of 5): FP8 at R = 8, H = 7168: T = 2048
-// -4.2 %, T = 4096 -3.4 %, T = 8192 -2.5 %; MXFP4 T = 4096 -3.4 %, T = 8192 -2.2 %; no
-// change at T <= 1024. The plain and small-call kernels hold 86-91 VGPRs, so two is
-// already their limit.
+// Workgroups per compute unit of the narrow shape of the FP8 and MXFP4 kernels at nvec in
+// (768, 1024] (7 or 8 waves per row) in the streaming schedule (T > 512): at most two. Their
+// registers (78 VGPRs) allow three, and two stream faster: reserving 56 KiB of LDS per
+// workgroup (of 160 KiB per compute unit), which the kernel does not use, leaves room for two.
+// Measured on MI355X (interleaved, median of 5, H = 7168), against no reservation: R = 8:
+// T = 1024 -1.4 %, T = 2048 -4.0 %, T = 8192 -2.7 .. -3.1 %; R = 6: -1.4 .. -3.8 %; R = 5 and
+// 4 from T = 2048: -1.0 .. -3.5 %, but +0.6 .. +5.9 % at T = 1024. The plain kernels and the
+// small-call schedule hold 86-91 VGPRs, so two is already their limit (a reservation there
+// measured 0 .. +1.3 %).
 constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
 
 unsigned lds_reserve(int R, int64_t T, int64_t H, Quant quant, int shape) {
     const int64_t nvec = H / 8;
-    const bool wide_two_slot = shape == FARN_VARIANT_BANDWIDTH && nvec > 768 && nvec <= 1024;
+    const bool long_row_narrow = shape == FARN_VARIANT_NARROW && nvec > 768 && nvec <= 1024;
     const bool streaming = T > farn::kSmallCallRows;
-    return (quant != kNone && wide_two_slot && streaming && (R >= 6 || (R >= 4 && T >= 2048))) ? kLdsTwoPerCu : 0u;
+    return (quant != kNone && long_row_narrow && streaming && (R >= 6 || (R >= 4 && T >= 2048))) ? kLdsTwoPerCu : 0u;
 }
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,
@@ -160,7 +161,7 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     const int variant = options & 0xff;
     const bool cols = (options & FARN_SCALES_COL_MAJOR) != 0;
     if ((options & ~(0xff | FARN_SCALES_COL_MAJOR)) != 0) return FARN_ERR_VARIANT;
-    if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_BANDWIDTH) return FARN_ERR_VARIANT;
+    if (variant < FARN_VARIANT_AUTO || variant > FARN_VARIANT_NARROW) return FARN_ERR_VARIANT;
     if (cols && quant != kFp8) return FARN_ERR_VARIANT;
     farn_status st = check(partials, R, residual, gamma, eps, T, H, group_size, quant,
                            residual_out, out, q, scales);
@@ -255,7 +256,7 @@ farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H
     c.T = T;
     c.H = H;
     c.residual_out = out;
-    return farn::launch(c, FARN_VARIANT_LATENCY) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, FARN_VARIANT_WIDE) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
@@ -269,7 +270,7 @@ farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size
     c.x = x;
     c.q = q;
     c.scales = scales;
-    return farn::launch(c, FARN_VARIANT_LATENCY) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
+    return farn::launch(c, FARN_VARIANT_WIDE) == 0 ? FARN_OK : FARN_ERR_LAUNCH;
 }
 
 farn_status farn_reduce_add_rmsnorm(const void *const *partials, int R, const void *residual,

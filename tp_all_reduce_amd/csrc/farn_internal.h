@@ -32,7 +32,7 @@ struct Call {
 };
 
 // Lanes per token row (= workgroup size) and 16-byte vectors per lane for hidden size
-// H and variant (1 = latency: widest mapping; 2 = bandwidth: about half the lanes,
+// H and variant (1 = wide: widest mapping; 2 = narrow: about half the lanes,
 // two vectors per lane).
 struct RowShape {
     int lanes;  // multiple of 64, <= 1024
@@ -44,7 +44,7 @@ RowShape row_shape(int64_t H, int variant);
 // on MI355X: faster up to T = 256, slower from T = 1024); above it, the streaming schedule.
 constexpr int64_t kSmallCallRows = 512;
 
-// Enqueue one workgroup per row. variant: 1 = latency, 2 = bandwidth (already resolved
+// Enqueue one workgroup per row. variant: 1 = wide, 2 = narrow (already resolved
 // from AUTO; the unfused blocks use 1). Returns 0 on success, nonzero when the launch failed.
 int launch(const Call &c, int variant);
 

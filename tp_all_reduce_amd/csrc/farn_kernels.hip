@@ -23,20 +23,20 @@
 //   normalisation product is fp64 too, rounded once to bf16. The row never passes
 //   through LDS; only one double per wave does.
 //
-// Two launch shapes of the same kernel (chosen by the host from T and H, as measured):
-//   latency   - the widest row mapping (L up to 1024, one vector per lane up to H =
-//               8192): the fewest instructions per lane.
-//   bandwidth - a narrow mapping (L about NV/2, two vectors per lane): half the waves
-//               per row, twice the loads in flight per lane. On MI355X it is the faster
-//               one for H = 7168 and 8192 (the FP8 prefill call at H = 7168: 212 against
-//               223 us) and, with two or four ranks, for mid-size and large T at
-//               H = 2048 .. 6144; at eight ranks the latency shape wins there.
-// The fp64 statistics make the two shapes agree bit for bit in practice (their sums
-// of squares differ only in the order of fp64 additions). The two-slot quant kernels
-// also have two store schedules, one for many rows and one for few (do_row). The host
-// may reserve LDS that the kernel does not use (Call::lds_reserve) to bound how many
-// workgroups share a compute unit: the plain two-slot kernel at H = 6152 .. 7168 streams
-// large T faster with two per compute unit than with the three its registers allow.
+// Two launch shapes of the same kernel (chosen by the host from R, T and H, as measured):
+//   wide   - the widest row mapping (L up to 1024, one vector per lane up to H = 8192): the
+//            fewest instructions per lane.
+//   narrow - L about NV/2, two vectors per lane: half the waves per row, twice the loads in
+//            flight per lane. On MI355X it is the faster one for H = 6152 .. 8192 (the FP8
+//            prefill call at H = 7168 by 3-4 %, decode by 5-9 %), at H = 4616 .. 5120 for
+//            1024 <= T < 2048, with up to four ranks at mid-size T, and for H <= 2048 from
+//            T = 4096.
+// The fp64 statistics make the two shapes agree bit for bit in practice (their sums of
+// squares differ only in the order of fp64 additions). The two-slot quant kernels also have
+// two store schedules, one for many rows and one for few (do_row). The host may reserve LDS
+// that the kernel does not use (Call::lds_reserve) to bound how many workgroups share a
+// compute unit: the streaming FP8 and MXFP4 two-slot kernels run faster at large T with two
+// per compute unit than with the three their registers allow.
 //
 // No MFMA: nothing here is a contraction; the op is HBM-bound (about 0.5 flop per
 // byte against a ridge of ~20 flop/byte).
