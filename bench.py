@@ -463,6 +463,9 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the message-size sweep (R=8, H=8192, T=2..4096), hot and cache-cold")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate the timed calls over buffer sets of >= 1 GiB in all (every call streams "
+                         "from HBM); for workloads that fit the last-level cache")
     ap.add_argument("--kernels", type=int, default=1, choices=(1, 2, 3),
                     help="time the FP8 step as the fused call (1), fused AR+RMSNorm then the quant (2), "
                          "or all-reduce, add+RMSNorm, quant (3); FP8 workloads only")
@@ -499,16 +502,23 @@ def main():
         log("copy calibration: 1 GiB read + 1 GiB written")
         del src, dst
 
+    # the buffer sets the timed loop rotates over: one, or (--cold) enough for >= 1 GiB, so
+    # that every call streams its inputs from HBM rather than the 256 MB last-level cache
+    sets = [bufs]
+    if args.cold:
+        sets += [bufs.clone(dev) for _ in range(max(1, -(-(1 << 30) // nb)) - 1)]
     settle_calls = 0
     if args.settle_ms > 0:
         t_end = time.perf_counter() + args.settle_ms / 1e3
         while time.perf_counter() < t_end:
-            for _ in range(10):
-                bufs.call(variant)
+            for i in range(10):
+                sets[(settle_calls + i) % len(sets)].call(variant)
             settle_calls += 10
             torch.cuda.synchronize()
-    log(f"timing {args.steps} steps after {settle_calls} settle calls and {args.warmup} warmup")
-    ms, wall_ms = time_calls([bufs], variant, args.steps, args.warmup)
+    log(f"timing {args.steps} steps after {settle_calls} settle calls and {args.warmup} warmup "
+        f"over {len(sets)} buffer set(s)")
+    ms, wall_ms = time_calls(sets, variant, args.steps, args.warmup)
+    del sets[1:]
     gbps = nb / (ms * 1e-3) / 1e9
     ran = F.select_variant(cfg.R, cfg.T, cfg.H, quant) if variant == F.VARIANT_AUTO else variant
     traffic = recorded_traffic(args.workload) if args.kernels == 1 else None
@@ -520,7 +530,8 @@ def main():
         "config": {"workload": describe(cfg, quant, emit_out), "name": args.workload, "R": cfg.R,
                    "T": cfg.T, "H": cfg.H, "quant": quant, "emit_bf16_out": emit_out,
                    "variant": {1: "latency", 2: "bandwidth"}[ran], "bytes_per_step": nb,
-                   "kernels_per_step": args.kernels, "seed": cfg.seed},
+                   "kernels_per_step": args.kernels, "buffer_sets": "rotated over >= 1 GiB" if args.cold else 1,
+                   "seed": cfg.seed},
         "us_per_call": round(ms * 1e3, 2), "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
         "settle_calls": settle_calls,
         "wall_us_per_call": round(wall_ms * 1e3, 2),
