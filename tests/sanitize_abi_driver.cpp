@@ -99,6 +99,37 @@ int main() {
     EXPECT(farn_reduce(parts, 2, 4, 256, A(0, 32), nullptr) == FARN_ERR_ALIAS);
     EXPECT(farn_quant_group(A(12), 4, 256, 128, A(12, 64), (float *)A(15), nullptr) == FARN_ERR_ALIAS);
     EXPECT(g_launches == before);
+    // LDS reserved to hold the streaming FP8 / MXFP4 kernels of long rows (H = 6152 .. 8192,
+    // narrow shape) at two workgroups per compute unit: R >= 6 above 512 rows, R = 4, 5 from
+    // 2048 rows; never for the plain call, the small-call schedule or the wide shape
+    struct LdsCase { int R; int64_t T, H; int quant; int variant; unsigned want; };
+    const LdsCase lds_cases[] = {
+        {8, 8192, 7168, 1, 0, 56u << 10}, {8, 8192, 7168, 2, 0, 56u << 10}, {8, 8192, 7168, 0, 0, 0},
+        {8, 512, 7168, 1, 0, 0},          {8, 513, 7168, 1, 0, 56u << 10}, {6, 1024, 6272, 1, 0, 56u << 10},
+        {5, 1024, 7168, 1, 0, 0},         {4, 2048, 7168, 1, 0, 56u << 10}, {4, 2047, 7168, 2, 0, 0},
+        {2, 8192, 7168, 1, 0, 0},         {8, 8192, 6144, 1, 0, 0},          {8, 8192, 8192, 1, 0, 56u << 10},
+        {8, 8192, 7168, 1, FARN_VARIANT_WIDE, 0}, {8, 8192, 8192, 0, FARN_VARIANT_NARROW, 0},
+    };
+    for (const LdsCase &lc : lds_cases) {
+        farn_status st;
+        if (lc.quant == 1)
+            st = farn_reduce_add_rmsnorm_quant_group_ex(parts, lc.R, A(10), A(11), eps, lc.T, lc.H, 128, B(12), B(13),
+                                                        B(14), (float *)B(15), nullptr, lc.variant);
+        else if (lc.quant == 2)
+            st = farn_reduce_add_rmsnorm_mxfp4_ex(parts, lc.R, A(10), A(11), eps, lc.T, lc.H, B(12), B(13), B(14),
+                                                  B(15), nullptr, lc.variant);
+        else
+            st = farn_reduce_add_rmsnorm_ex(parts, lc.R, A(10), A(11), eps, lc.T, lc.H, B(12), B(13), nullptr,
+                                            lc.variant);
+        if (st != FARN_OK)
+            fprintf(stderr, "R=%d T=%lld H=%lld quant=%d: status %d\n", lc.R, (long long)lc.T, (long long)lc.H, lc.quant,
+                    (int)st);
+        EXPECT(st == FARN_OK);
+        if (g_last.lds_reserve != lc.want)
+            fprintf(stderr, "lds_reserve R=%d T=%lld H=%lld quant=%d variant=%d: %u, want %u\n", lc.R, (long long)lc.T,
+                    (long long)lc.H, lc.quant, lc.variant, g_last.lds_reserve, lc.want);
+        EXPECT(g_last.lds_reserve == lc.want);
+    }
     // the dispatch rule and the status strings over a grid, extreme sizes included
     const int64_t Ts[] = {1, 2, 63, 64, 511, 512, 1023, 1024, 2047, 2048, 4096, 8191, 8192, (int64_t)1 << 40};
     for (int R = 1; R <= 8; ++R)
