@@ -1,7 +1,8 @@
 /*
  * Test kernels for the GPU conversion instructions the FP8 and MXFP4 paths rely on
  * (tests/test_gpu_conversions.py): v_cvt_pk_fp8_f32 over a range of fp32 bit patterns,
- * and v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent.
+ * v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent, and the
+ * fused kernels' reciprocal square root (v_rsq_f64 and one Newton step).
  * Built by tp_all_reduce_amd/build.py; not part of the library.
  */
 #include <hip/hip_runtime.h>
@@ -27,6 +28,24 @@ __global__ void fp4_all_scales(const float *x, uint8_t *out, uint32_t n) {
     const size_t base = (size_t)blockIdx.y * n;
     out[base + 2 * i] = (uint8_t)(w & 0xfu);
     out[base + 2 * i + 1] = (uint8_t)((w >> 4) & 0xfu);
+}
+
+// out[i] = 1/sqrt(m[i]) as the fused kernels form it for 2^-1000 <= m <= 2^1000: the hardware
+// reciprocal square root (v_rsq_f64) refined by one Newton step
+__global__ void rsq_newton(const double *m, double *out, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const double x = m[i];
+    const double y0 = __builtin_amdgcn_rsq(x);
+    const double e = __builtin_fma(-0.5 * x * y0, y0, 0.5);
+    out[i] = __builtin_fma(y0, e, y0);
+}
+
+extern "C" int hwconv_rsq_newton(const void *m, void *out, uint32_t n, void *stream) {
+    if (n == 0 || n > (1u << 26)) return 1;
+    const uint32_t block = 256, grid = (n + block - 1) / block;
+    hipLaunchKernelGGL(rsq_newton, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const double *)m, (double *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 extern "C" int hwconv_fp8_of_bits(uint32_t base, void *out, uint32_t n, void *stream) {

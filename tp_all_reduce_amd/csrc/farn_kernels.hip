@@ -20,8 +20,9 @@
 //   (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
 //   per wave through LDS -> every wave adds the per-wave values in wave order; the
-//   normalisation product is fp64 too, rounded once to bf16. The row never passes
-//   through LDS; only one double per wave does.
+//   normalisation product is rounded once to bf16 (formed in fp32 where that provably
+//   gives the same value, else in fp64). The row never passes through LDS; only one
+//   double per wave does.
 //
 // Two launch shapes of the same kernel (chosen by the host from R, T and H, as measured):
 //   wide   - the widest row mapping (L up to 1024, one vector per lane up to H = 8192): the
