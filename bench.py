@@ -63,7 +63,15 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source's code: comments, blank lines and trailing blanks
+    removed, so that recorded counters stay tied to the code they were taken on and not to
+    its comments."""
+    import re
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def describe(cfg, quant, emit_out):
