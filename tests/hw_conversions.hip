@@ -2,7 +2,7 @@
  * Test kernels for the GPU conversion instructions the FP8 and MXFP4 paths rely on
  * (tests/test_gpu_conversions.py): v_cvt_pk_fp8_f32 over a range of fp32 bit patterns,
  * v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent, and the
- * fused kernels' reciprocal square root (v_rsq_f64 and one Newton step).
+ * fused kernels' reciprocal square root (v_rsq_f64 and two Newton steps).
  * Built by tp_all_reduce_amd/build.py; not part of the library.
  */
 #include <hip/hip_runtime.h>
@@ -30,15 +30,17 @@ __global__ void fp4_all_scales(const float *x, uint8_t *out, uint32_t n) {
     out[base + 2 * i + 1] = (uint8_t)((w >> 4) & 0xfu);
 }
 
-// out[i] = 1/sqrt(m[i]) as the fused kernels form it for 2^-1000 <= m <= 2^1000: the hardware
-// reciprocal square root (v_rsq_f64) refined by one Newton step
+// out[2i] = the hardware reciprocal square root (v_rsq_f64) of m[i], out[2i+1] = 1/sqrt(m[i]) as
+// the fused kernels form it for 2^-1000 <= m <= 2^1000: v_rsq_f64 refined by two Newton steps
 __global__ void rsq_newton(const double *m, double *out, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const double x = m[i];
+    const double hm = 0.5 * x;
     const double y0 = __builtin_amdgcn_rsq(x);
-    const double e = __builtin_fma(-0.5 * x * y0, y0, 0.5);
-    out[i] = __builtin_fma(y0, e, y0);
+    const double y1 = __builtin_fma(y0, __builtin_fma(-hm * y0, y0, 0.5), y0);
+    out[2 * i] = y0;
+    out[2 * i + 1] = __builtin_fma(y1, __builtin_fma(-hm * y1, y1, 0.5), y1);
 }
 
 extern "C" int hwconv_rsq_newton(const void *m, void *out, uint32_t n, void *stream) {

@@ -608,6 +608,32 @@ def test_random_shapes(dev):
             run_mxfp4(u, variant, emit_out=bool(i % 2), label=f"rand{i}")
 
 
+# one point inside every band of the automatic shape rule (and the reserved-LDS launches), and
+# points just outside them: (R, T, H)
+RULE_BAND_POINTS = [
+    (8, 64, 6272), (8, 600, 7168), (6, 2100, 7168), (4, 2048, 6656), (8, 4096, 8192), (8, 3000, 8192),
+    (8, 1024, 5120), (2, 1500, 4736), (8, 2048, 5120), (4, 600, 2304), (2, 1500, 3072), (4, 1024, 4096),
+    (3, 700, 6144), (8, 4096, 2048), (8, 4200, 1664), (8, 4096, 1536), (5, 520, 7168), (1, 513, 8192),
+]
+
+
+@pytest.mark.parametrize("R,T,H", RULE_BAND_POINTS)
+def test_rule_bands(dev, R, T, H):
+    """Every band of the automatic launch-shape rule, with the LDS reservation where it applies,
+    against the oracle on every row, through the plain, FP8 and MXFP4 calls."""
+    d = make_inputs(CONFIGS["decode_fp8"], seed=3000 + R * 7 + T + H, R=R, T=T, H=H)
+    u = Uploaded(d, dev, residual=bool((T + H) % 3))
+    ref = u.oracle_rows(np.arange(T), False)
+    rep_ro, rep_out, _ = run_and_compare(u, False, "auto", label="band", ref=ref)
+    assert rep_ro["n_bit_diff"] == 0 and rep_out["n_bit_diff"] == 0
+    if H % 128 == 0:
+        _, rep_out, rep_fp8 = run_and_compare(u, True, "auto", label="band")
+        assert rep_out["n_bit_diff"] == 0 and rep_fp8["n_code_diff"] == 0 and rep_fp8["max_scale_rel_err"] == 0.0
+    if H % 32 == 0:
+        rep = run_mxfp4(u, "auto", label="band")
+        assert rep["n_code_diff"] == 0 and rep["n_scale_diff"] == 0
+
+
 def test_two_streams_at_once(dev):
     """The library keeps no state: calls enqueued on two streams at the same time, on different
     inputs (one FP8, one plain, one MXFP4 per stream, back to back), each match the oracle."""

@@ -312,11 +312,12 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
 // and when that element is a group's amax its scale moves by up to 2^-7); MI355X runs
 // fp64 vector FMAs at the rate of unpacked fp32 ones.
 // m is formed as ss * (1/H) + eps by one FMA, and 1/sqrt(m) as the hardware reciprocal
-// square root refined by one Newton step (y += y * (1/2 - m y^2 / 2)): both sit within
-// about an fp64 unit of the correctly rounded quotient and root, far below what the bf16
-// outputs resolve, and the row's dependent chain after the barrier is some 30 fp64
-// operations shorter than with a division and a square root. Outside 2^-1000 <= m <=
-// 2^1000 (and for an inf or NaN m) the division and square root are used.
+// square root (about 24 correct bits, measured) refined by two Newton steps
+// (y += y * (1/2 - m y^2 / 2)): the result sits within two fp64 units of the correctly
+// rounded 1/sqrt (one step leaves up to ~20), far below what the bf16 outputs resolve, and
+// the row's dependent chain after the barrier is some 25 fp64 operations shorter than with a
+// division and a square root. Outside 2^-1000 <= m <= 2^1000 (and for an inf or NaN m) the
+// division and square root are used.
 __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *slot) {
     const int lane = (int)threadIdx.x & 63;
     const int wave = (int)threadIdx.x >> 6;
@@ -329,9 +330,10 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     const double m = __builtin_fma(tot, k.inv_h, (double)k.eps);
     double r;
     if (m >= 0x1p-1000 && m <= 0x1p1000) {  // the same in every lane of the row
+        const double hm = 0.5 * m;
         const double y0 = __builtin_amdgcn_rsq(m);
-        const double e = __builtin_fma(-0.5 * m * y0, y0, 0.5);
-        r = __builtin_fma(y0, e, y0);
+        const double y1 = __builtin_fma(y0, __builtin_fma(-hm * y0, y0, 0.5), y0);
+        r = __builtin_fma(y1, __builtin_fma(-hm * y1, y1, 0.5), y1);
     } else {
         __asm__ volatile("" ::: "memory");  // keeps this rare path a branch, not computed beside the other
         r = 1.0 / __builtin_sqrt(tot / k.h + (double)k.eps);
