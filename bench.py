@@ -55,7 +55,8 @@ WORKLOADS = {
 for _T in SWEEP_T:
     WORKLOADS[f"sweep_T{_T}"] = (sweep_config(_T), False, True)
 
-VARIANT_NAMES = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
+VARIANT_NAMES = {"auto": F.VARIANT_AUTO, "wide": F.VARIANT_WIDE, "narrow": F.VARIANT_NARROW,
+                 "latency": F.VARIANT_WIDE, "bandwidth": F.VARIANT_NARROW}
 
 
 def log(msg):
@@ -416,7 +417,7 @@ def sweep(dev):
         # both launch shapes forced, timed right after (hot), as the dispatch rule was set; before
         # the cold leg, whose rotation over 1 GiB leaves the caches in another state
         forced = {name: round(median_graph([b], v, 200, 10) * 1e3, 2)
-                  for name, v in (("latency", F.VARIANT_LATENCY), ("bandwidth", F.VARIANT_BANDWIDTH))}
+                  for name, v in (("wide", F.VARIANT_WIDE), ("narrow", F.VARIANT_NARROW))}
         k = max(1, -(-(1 << 30) // nb))
         sets = [b] + [b.clone(dev) for _ in range(k - 1)]
         calls = k * max(1, 200 // k)
@@ -424,13 +425,70 @@ def sweep(dev):
         gbps = nb / (cold * 1e-3) / 1e9
         pt = {"T": T, "bytes": nb, "hot_us": round(hot * 1e3, 2), "cold_us": round(cold * 1e3, 2),
               "cold_GBps": round(gbps, 1), "cold_pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
-              "shape": {1: "latency", 2: "bandwidth"}[F.select_variant(cfg.R, T, cfg.H, False)],
+              "shape": {1: "wide", 2: "narrow"}[F.select_variant(cfg.R, T, cfg.H, False)],
               "forced_hot_us": forced, "rotation_sets": k}
         out["points"].append(pt)
         log(f"sweep T={T}: {pt}")
         del sets, b
         torch.cuda.empty_cache()
     return out
+
+
+def shape_points(n, seed):
+    """n random call shapes, seeded: R in 2..8, H a multiple of 128 in 1024..8192, T log-uniform
+    over 16..8192, plain / FP8 / MXFP4 calls (45 / 35 / 20 %), at most 3 GiB of inputs and
+    outputs per call."""
+    rng = np.random.default_rng(seed)
+    pts = []
+    while len(pts) < n:
+        R = int(rng.integers(2, 9))
+        H = int(rng.integers(8, 65)) * 128
+        T = int(np.exp(rng.uniform(np.log(16), np.log(8192))))
+        u = rng.random()
+        quant = False if u < 0.45 else (True if u < 0.8 else "mxfp4")
+        if (R + 3) * T * H * 2 <= (3 << 30):
+            pts.append((R, H, T, quant))
+    return pts
+
+
+def shapes_check(dev, n, seed):
+    """Both launch shapes forced at n random call shapes (graph replay, interleaved, median of
+    5; cache-hot for calls up to 128 MiB, buffer sets rotated over >= 1 GiB above), and what the
+    automatic rule loses at each against the faster of the two."""
+    points = []
+    for (R, H, T, quant) in shape_points(n, seed):
+        cfg = Config("shape", R=R, T=T, H=H, quant=(False,))
+        b = Bufs(make_inputs(cfg, seed=R * 1000 + T + H), dev, quant, True)
+        nb = nbytes(cfg, quant, True)
+        us_est = max(3.0, nb / 6.0e12 * 1e6)
+        if nb <= (128 << 20):
+            sets, calls, replays = [b], max(10, min(200, int(8000 / us_est))), 5
+        else:
+            k = max(1, -(-(1 << 30) // nb))
+            sets = [b] + [b.clone(dev) for _ in range(k - 1)]
+            calls = k * max(1, int(8000 / us_est) // k)
+            replays = max(2, int(20000 / (us_est * calls)))
+        t = {F.VARIANT_WIDE: [], F.VARIANT_NARROW: []}
+        for _ in range(5):
+            for v in t:
+                t[v].append(time_graph(sets, v, calls, replays))
+        w, nr = (statistics.median(t[v]) * 1e3 for v in (F.VARIANT_WIDE, F.VARIANT_NARROW))
+        auto = F.select_variant(R, T, H, quant)
+        pt = {"R": R, "H": H, "T": T, "quant": {False: "plain", True: "fp8"}.get(quant, quant),
+              "wide_us": round(w, 3), "narrow_us": round(nr, 3), "auto": {1: "wide", 2: "narrow"}[auto],
+              "auto_loss_pct": round(100 * ((w if auto == F.VARIANT_WIDE else nr) / min(w, nr) - 1), 2)}
+        points.append(pt)
+        log(f"shapes: {pt}")
+        del sets, b
+        torch.cuda.empty_cache()
+    losses = sorted((p["auto_loss_pct"] for p in points), reverse=True)
+    return {"what": "both launch shapes at random call shapes; auto_loss_pct = the automatic rule's "
+                    "time over the faster shape's, in per cent",
+            "seed": seed, "points": len(points), "auto_loss_mean_pct": round(statistics.mean(losses), 3),
+            "auto_loss_max_pct": losses[0], "points_over_5pct": sum(1 for x in losses if x > 5),
+            "always_wide_loss_mean_pct": round(statistics.mean(
+                100 * (p["wide_us"] / min(p["wide_us"], p["narrow_us"]) - 1) for p in points), 3),
+            "detail": points}
 
 
 def unfused(dev):
@@ -477,6 +535,10 @@ def main():
     ap.add_argument("--kernels", type=int, default=1, choices=(1, 2, 3),
                     help="time the FP8 step as the fused call (1), fused AR+RMSNorm then the quant (2), "
                          "or all-reduce, add+RMSNorm, quant (3); FP8 workloads only")
+    ap.add_argument("--shapes", type=int, default=0, metavar="N",
+                    help="instead of the bench: time both launch shapes at N random call shapes and "
+                         "report what the automatic rule loses against the faster one (one JSON line)")
+    ap.add_argument("--shapes-seed", type=int, default=13)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one torch copy of 1 GiB (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -489,6 +551,9 @@ def main():
         print("bench.py needs the GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.shapes > 0:
+        print(json.dumps({"shapes_check": shapes_check(dev, args.shapes, args.shapes_seed)}), flush=True)
+        return
     cfg, quant, emit_out = WORKLOADS[args.workload]
     variant = VARIANT_NAMES[args.variant]
     if args.kernels != 1 and not (quant is True and emit_out):
@@ -537,7 +602,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(cfg, quant, emit_out), "name": args.workload, "R": cfg.R,
                    "T": cfg.T, "H": cfg.H, "quant": quant, "emit_bf16_out": emit_out,
-                   "variant": {1: "latency", 2: "bandwidth"}[ran], "bytes_per_step": nb,
+                   "variant": {1: "wide", 2: "narrow"}[ran], "bytes_per_step": nb,
                    "kernels_per_step": args.kernels, "buffer_sets": "rotated over >= 1 GiB" if args.cold else 1,
                    "seed": cfg.seed},
         "us_per_call": round(ms * 1e3, 2), "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 1),
@@ -550,7 +615,7 @@ def main():
                          "recorded rocprofv3 FETCH_SIZE + WRITE_SIZE counters of this kernel source (sha256[:16] "
                          f"{kernel_hash()}), scaled by a 1 GiB copy, in profiles/traffic.json; HBM bytes per "
                          "launch / this run's time per launch"),
-                     "kernel": "farn_rows (" + {1: "latency", 2: "bandwidth"}[ran] + " shape)"
+                     "kernel": "farn_rows (" + {1: "wide", 2: "narrow"}[ran] + " shape)"
                                + ("" if args.kernels == 1 else f" + {args.kernels - 1} unfused kernel(s)"),
                      "kernel_sha": kernel_hash(),
                      "algorithmic_bytes_per_launch": nb,

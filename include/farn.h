@@ -81,7 +81,7 @@ typedef enum farn_status {
 #define FARN_GROUP 128
 /* MXFP4 block along H (OCP Microscaling Formats (MX) v1.0: 32 elements per shared scale). */
 #define FARN_MX_BLOCK 32
-#define FARN_ABI_VERSION 3
+#define FARN_ABI_VERSION 4
 
 /*
  * Plain call: reduce + residual add + RMSNorm.
@@ -142,9 +142,9 @@ farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, co
  * The older names describe launch widths, not regimes: both shapes serve every T. AUTO
  * (farn_select_variant) picks by measurement on MI355X. It takes NARROW for
  *   - 6144 < H <= 8192, except the plain call with H > 7168 from T = 4096;
- *   - 4608 < H <= 5120 with 1024 <= T < 2048;
- *   - R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048);
- *   - 1536 < H <= 2048 from T = 4096;
+ *   - 4608 < H <= 5120 with 768 <= T < 2048;
+ *   - the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512;
+ *   - R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536);
  * and WIDE everywhere else. Both compute the same results (their fp64 sums of squares differ
  * only in the order of additions). */
 typedef enum farn_variant {
@@ -201,7 +201,8 @@ farn_status farn_reduce(const void *const *partials, int R, int64_t T, int64_t H
 farn_status farn_quant_group(const void *x, int64_t T, int64_t H, int group_size, void *q,
                              float *scales, void *stream);
 
-/* The variant AUTO would run for this shape (no validation; pure function of its arguments). */
+/* The variant AUTO would run for this shape (no validation; pure function of its arguments).
+ * quant: 0 for the plain call, 1 for the FP8 call, 2 for the MXFP4 call. */
 int farn_select_variant(int R, int64_t T, int64_t H, int quant);
 
 /* Static, NUL-terminated description of a status code. */

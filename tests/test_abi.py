@@ -63,23 +63,27 @@ def test_status_strings_and_select():
 W, N = F.VARIANT_WIDE, F.VARIANT_NARROW
 # Every band of the AUTO rule as include/farn.h states it, at its edges: (R, T, H, quant, shape)
 HEADER_RULE_POINTS = [
-    # 6144 < H <= 8192: narrow, except the plain call with H > 7168 from T = 4096
+    # 6144 < H <= 8192, except the plain call with H > 7168 from T = 4096
     (8, 1, 6152, False, N), (8, 64, 7168, False, N), (8, 8192, 7168, False, N), (8, 8192, 7168, True, N),
     (2, 8192, 7168, False, N), (8, 64, 8192, False, N), (8, 4095, 8192, False, N), (8, 4096, 8192, False, W),
     (8, 8192, 8192, False, W), (2, 4096, 8192, False, W), (8, 8192, 8192, True, N), (8, 4096, 7176, False, W),
-    (8, 4096, 7168, False, N), (8, 64, 6144, False, W),
-    # 4608 < H <= 5120 with 1024 <= T < 2048
-    (8, 1024, 5120, False, N), (8, 2047, 4616, True, N), (8, 1023, 5120, False, W), (8, 2048, 5120, False, W),
-    (8, 1024, 4608, False, W), (8, 1024, 5128, False, W),
-    # R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048)
-    (4, 512, 2056, False, N), (4, 1023, 6144, True, N), (4, 1024, 4096, False, W), (4, 511, 3072, False, W),
-    (2, 1024, 4096, False, N), (2, 2047, 3072, True, N), (2, 2048, 3072, False, W), (1, 512, 4096, False, N),
-    (5, 512, 3072, False, W), (4, 512, 2048, False, W), (4, 512, 6152, False, N), (4, 512, 6160, False, N),
-    # 1536 < H <= 2048 from T = 4096
-    (8, 4096, 2048, False, N), (8, 8192, 1544, True, N), (8, 4095, 2048, False, W), (8, 8192, 1536, False, W),
-    # everything else: wide
-    (8, 64, 4096, False, W), (8, 8192, 4096, True, W), (8, 8192, 6144, False, W), (8, 1024, 2048, False, W),
-    (4, 16, 4096, True, W), (8, 4, 256, False, W), (2, 8192, 32768, False, W),
+    (8, 4096, 7168, False, N), (8, 64, 6144, False, W), (8, 8192, 8192, "mxfp4", N), (8, 64, 7168, "mxfp4", N),
+    # 4608 < H <= 5120 with 768 <= T < 2048
+    (8, 768, 5120, False, N), (8, 2047, 4616, True, N), (8, 767, 5120, False, W), (8, 2048, 5120, False, W),
+    (8, 1024, 4608, False, W), (8, 1024, 5128, False, W), (6, 1000, 4736, "mxfp4", N), (8, 767, 5120, True, W),
+    # the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512
+    (8, 16, 2560, True, N), (8, 16, 2560, False, W), (8, 16, 2560, "mxfp4", W), (8, 767, 3712, True, N),
+    (8, 768, 3712, True, W), (8, 100, 3720, True, W), (8, 256, 6144, True, N), (8, 511, 4096, True, N),
+    (8, 512, 4096, True, W), (8, 255, 4096, True, W), (8, 300, 2048, True, W), (8, 300, 2056, True, N),
+    (1, 1, 2056, True, N), (6, 300, 4096, "fp8", N), (6, 300, 4096, "mxfp4", W),
+    # R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536)
+    (4, 512, 2056, False, N), (4, 767, 6144, False, N), (4, 768, 4096, False, W), (4, 511, 3072, False, W),
+    (2, 1535, 4096, False, N), (2, 1536, 3072, False, W), (1, 512, 4096, False, N), (5, 512, 3072, False, W),
+    (4, 512, 2048, False, W), (3, 600, 6144, "mxfp4", N), (2, 1024, 4096, "mxfp4", N), (4, 700, 6144, True, N),
+    # everything else: wide (H = 1544 .. 2048 from T = 4096 included)
+    (8, 4096, 2048, False, W), (8, 8192, 1544, True, W), (8, 64, 4096, False, W), (8, 8192, 4096, True, W),
+    (8, 8192, 6144, False, W), (8, 1024, 2048, False, W), (4, 16, 4096, True, W), (8, 4, 256, False, W),
+    (2, 8192, 32768, False, W), (2, 8192, 32768, "mxfp4", W),
 ]
 
 
@@ -92,9 +96,10 @@ def test_select_matches_header(R, T, H, quant, shape):
 def test_header_states_the_rule():
     text = open(HEADER).read()
     for phrase in ("6144 < H <= 8192, except the plain call with H > 7168 from T = 4096",
-                   "4608 < H <= 5120 with 1024 <= T < 2048",
-                   "R <= 4 and 2048 < H <= 6144 with 512 <= T < 1024 (R <= 2: T < 2048)",
-                   "1536 < H <= 2048 from T = 4096", "and WIDE everywhere else"):
+                   "4608 < H <= 5120 with 768 <= T < 2048",
+                   "the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512",
+                   "R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536)",
+                   "and WIDE everywhere else", "quant: 0 for the plain call, 1 for the FP8 call, 2 for the MXFP4 call"):
         assert phrase in " ".join(text.replace("*", " ").split()), phrase
 
 

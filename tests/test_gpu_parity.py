@@ -25,7 +25,7 @@ from parity import (compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16, mxf
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
-VARIANTS = {"auto": F.VARIANT_AUTO, "latency": F.VARIANT_LATENCY, "bandwidth": F.VARIANT_BANDWIDTH}
+VARIANTS = {"auto": F.VARIANT_AUTO, "wide": F.VARIANT_WIDE, "narrow": F.VARIANT_NARROW}
 # oracle threads: the host cores this process may run on, at most 16
 ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -122,7 +122,7 @@ def _prefill_ref(u, kind):
 
 
 @pytest.mark.parametrize("quant", [False, True])
-@pytest.mark.parametrize("variant", ["auto", "latency", "bandwidth"])
+@pytest.mark.parametrize("variant", ["auto", "wide", "narrow"])
 def test_prefill_full_size_all_rows(prefill, quant, variant):
     rep = run_and_compare(prefill, quant, variant, label="prefill, every row",
                           ref=_prefill_ref(prefill, "fp8" if quant else "plain"))
@@ -130,12 +130,12 @@ def test_prefill_full_size_all_rows(prefill, quant, variant):
 
 
 def test_prefill_full_size_properties(prefill):
-    """Whole-tensor checks at full size: the latency and bandwidth launch shapes agree bit for
+    """Whole-tensor checks at full size: the wide and narrow launch shapes agree bit for
     bit on every row (their fp64 sums of squares differ only in addition order), and every
     output is finite."""
     say("[gpu] prefill whole-tensor variant identity")
-    a = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_LATENCY)
-    b = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    a = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_WIDE)
+    b = F.reduce_add_rmsnorm_quant_group(prefill.P, prefill.res, prefill.g, EPS, variant=F.VARIANT_NARROW)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
@@ -146,16 +146,16 @@ def test_prefill_full_size_properties(prefill):
 
 @pytest.mark.parametrize("R,H", [(6, 7168), (8, 6656)])
 def test_two_workgroups_per_cu_launch(dev, R, H):
-    """The plain call's bandwidth shape at H = 6152..7168 with R >= 6 and T >= 2048 is launched
+    """The plain call's narrow shape at H = 6152..7168 with R >= 6 and T >= 2048 is launched
     with LDS reserved so that at most two workgroups share a compute unit: its outputs match the
-    oracle on every row, and the latency shape (launched without the reservation) bit for bit
+    oracle on every row, and the wide shape (launched without the reservation) bit for bit
     on every row."""
     T = 2048
     u = Uploaded(make_inputs(CONFIGS["prefill"], seed=40 + R, R=R, T=T, H=H), dev)
-    assert F.select_variant(R, T, H, False) == F.VARIANT_BANDWIDTH
+    assert F.select_variant(R, T, H, False) == F.VARIANT_NARROW
     run_and_compare(u, False, "auto", label="two-per-CU")
-    a = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_BANDWIDTH)
-    b = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_LATENCY)
+    a = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_NARROW)
+    b = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, variant=F.VARIANT_WIDE)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
@@ -192,7 +192,7 @@ def test_edge_H(dev, H):
 @pytest.mark.parametrize("R", list(range(1, 9)))
 def test_edge_R(dev, R):
     u = Uploaded(make_inputs(CONFIGS["tiny"], seed=R, R=R, T=7, H=1024), dev)
-    for variant in ("latency", "bandwidth"):
+    for variant in ("wide", "narrow"):
         run_and_compare(u, False, variant, label=f"R{R}")
         run_and_compare(u, True, variant, label=f"R{R}")
 
@@ -219,7 +219,7 @@ def test_quant_without_bf16_out(dev):
 def test_in_place_residual(dev):
     d = make_inputs(CONFIGS["decode_ds"], seed=10, T=33)
     ref_ro, ref_out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
-    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
         say(f"[gpu] in-place residual variant={variant}")
         u = Uploaded(d, dev)
         ro, out = F.reduce_add_rmsnorm(u.P, u.res, u.g, EPS, residual_out=u.res, variant=variant)
@@ -237,7 +237,7 @@ def test_in_place_residual_quant(dev):
     d = make_inputs(CONFIGS["decode_ds"], seed=11, T=21)
     ref = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
     ref_mx = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
-    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
         say(f"[gpu] in-place residual, FP8 and MXFP4, variant={variant}")
         u = Uploaded(d, dev)
         ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, residual_out=u.res, variant=variant)
@@ -314,7 +314,7 @@ def test_subnormal_and_tiny_values(dev):
     d["partials"] = P
     d["residual"] = np.zeros_like(d["residual"])
     u = Uploaded(d, dev)
-    for variant in ("latency", "bandwidth"):
+    for variant in ("wide", "narrow"):
         run_and_compare(u, False, variant, label="subnormal")
         run_and_compare(u, True, variant, label="subnormal")
 
@@ -345,7 +345,7 @@ def test_tiny_scale_groups(dev):
     d = make_inputs(CONFIGS["tiny"], seed=71, R=2, T=8, H=1024)
     d["gamma"] = _with_group_exponents(d["gamma"][None, :], TINY_GROUP_EXPONENTS, rng)[0]
     u = Uploaded(d, dev)
-    for variant in ("latency", "bandwidth"):
+    for variant in ("wide", "narrow"):
         _, _, rep = run_and_compare(u, True, variant, label="tiny-scale groups")
         assert rep["n_code_diff"] == 0 and rep["max_scale_rel_err"] == 0.0, rep
     x = _with_group_exponents(make_inputs(CONFIGS["tiny"], seed=72, R=1, T=16, H=1024)["residual"],
@@ -397,7 +397,7 @@ def test_signed_zeros_bit_exact(dev):
     ref = u.oracle_rows(np.arange(5), True)
     ref_mx = oracle.reduce_add_rmsnorm_mxfp4(P, res, d["gamma"], EPS, nthreads=4)
     assert (ref[1] == 0x8000).sum() >= 400 and (ref[2][4] == 0x80).sum() >= 1000
-    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
         say(f"[gpu] signed zeros, variant={variant}")
         ro, out, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant)
         mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, variant=variant)
@@ -543,7 +543,7 @@ def test_mxfp4_configs(dev, name, variant):
     assert rep["n_code_diff"] == 0 and rep["n_scale_diff"] == 0  # bit-exact in practice
 
 
-@pytest.mark.parametrize("variant", ["auto", "latency", "bandwidth"])
+@pytest.mark.parametrize("variant", ["auto", "wide", "narrow"])
 def test_mxfp4_prefill_all_rows(prefill, variant):
     rep = run_mxfp4(prefill, variant, label="prefill, every row", ref=_prefill_ref(prefill, "mxfp4"))
     say(f"[gpu]   {rep}")
@@ -577,7 +577,7 @@ def test_fp8_scales_column_major(dev, name):
     u = Uploaded(make_inputs(CONFIGS[name], seed=95), dev)
     say(f"[gpu] column-major scales {name}")
     r_ro, r_out, r_q, r_s = u.oracle_rows(np.arange(u.T), True)
-    for variant in (F.VARIANT_LATENCY, F.VARIANT_BANDWIDTH):
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
         a = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant)
         b = F.reduce_add_rmsnorm_quant_group(u.P, u.res, u.g, EPS, variant=variant, scales_col_major=True)
         torch.cuda.synchronize()
@@ -600,7 +600,7 @@ def test_random_shapes(dev):
         H = int(rng.integers(1, 129)) * 128 if i % 3 else int(rng.integers(1, 2049)) * 8
         d = make_inputs(CONFIGS["decode_fp8"], seed=1000 + i, R=R, T=T, H=H)
         u = Uploaded(d, dev, residual=bool(i % 4))
-        variant = ["auto", "latency", "bandwidth"][i % 3]
+        variant = ["auto", "wide", "narrow"][i % 3]
         run_and_compare(u, False, variant, label=f"rand{i}")
         if H % 128 == 0:
             run_and_compare(u, True, variant, emit_out=bool(i % 2), label=f"rand{i}")
@@ -614,6 +614,8 @@ RULE_BAND_POINTS = [
     (8, 64, 6272), (8, 600, 7168), (6, 2100, 7168), (4, 2048, 6656), (8, 4096, 8192), (8, 3000, 8192),
     (8, 1024, 5120), (2, 1500, 4736), (8, 2048, 5120), (4, 600, 2304), (2, 1500, 3072), (4, 1024, 4096),
     (3, 700, 6144), (8, 4096, 2048), (8, 4200, 1664), (8, 4096, 1536), (5, 520, 7168), (1, 513, 8192),
+    (8, 800, 4736), (6, 300, 3328), (8, 100, 2560), (7, 400, 5504), (4, 700, 4096), (2, 1300, 4096),
+    (8, 767, 3712),
 ]
 
 
@@ -683,15 +685,15 @@ def test_plain_c_client():
 def test_small_and_streaming_schedules_agree(dev, quant):
     """The two-slot quant kernels store in a different order for few rows (T <= 512) than for
     many; results must not depend on it. The same 512 rows run as a 512-row call (small-call
-    schedule) and inside a 520-row call (streaming schedule), bandwidth shape, and every output
+    schedule) and inside a 520-row call (streaming schedule), narrow shape, and every output
     byte of those rows must agree; the small call is also checked against the oracle."""
     d = make_inputs(CONFIGS["decode_ds"], seed=77, T=520)
     u = Uploaded(d, dev)
     P512 = [p[:512] for p in u.P]
     call = F.reduce_add_rmsnorm_quant_group if quant == "fp8" else F.reduce_add_rmsnorm_mxfp4
     say(f"[gpu] schedules agree ({quant}): T=512 vs T=520")
-    big = call(u.P, u.res, u.g, EPS, variant=F.VARIANT_BANDWIDTH)
-    small = call(P512, u.res[:512], u.g, EPS, variant=F.VARIANT_BANDWIDTH)
+    big = call(u.P, u.res, u.g, EPS, variant=F.VARIANT_NARROW)
+    small = call(P512, u.res[:512], u.g, EPS, variant=F.VARIANT_NARROW)
     torch.cuda.synchronize()
     for a, b in zip(small, big):
         assert torch.equal(a.view(torch.uint8), b[:512].contiguous().view(torch.uint8))
@@ -819,12 +821,12 @@ def test_rows_beyond_one_dispatch(dev):
         assert np.array_equal(Q[idx].cpu().numpy(), rq)
         assert np.array_equal(S.view(T, G)[idx].cpu().numpy(), rs)
 
-        say("[gpu]   fused FP8, latency shape, column-major scales")
+        say("[gpu]   fused FP8, wide shape, column-major scales")
         B.view(torch.int16).fill_(-1)
         Q.fill_(0xFF)
         S.fill_(float("nan"))
         F.reduce_add_rmsnorm_quant_group([A], None, g, EPS, emit_out=False, residual_out=B, q=Q,
-                                         scales=S, variant=F.VARIANT_LATENCY, scales_col_major=True)
+                                         scales=S, variant=F.VARIANT_WIDE, scales_col_major=True)
         torch.cuda.synchronize()
         r_ro, _, r_q, r_s = oracle.reduce_add_rmsnorm_quant_group(src[None], None, d["gamma"], EPS,
                                                                   emit_out=False)

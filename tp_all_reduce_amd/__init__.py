@@ -81,8 +81,11 @@ def abi_version() -> int:
     return _lib.farn_abi_version()
 
 
-def select_variant(R: int, T: int, H: int, quant: bool) -> int:
-    return _lib.farn_select_variant(R, T, H, int(bool(quant)))
+def select_variant(R: int, T: int, H: int, quant=False) -> int:
+    """The launch shape AUTO runs; quant: False for the plain call, True or "fp8" for the FP8
+    call, "mxfp4" for the MXFP4 call."""
+    kind = 2 if isinstance(quant, str) and quant == "mxfp4" else (1 if quant else 0)
+    return _lib.farn_select_variant(R, T, H, kind)
 
 
 _BF16 = torch.bfloat16

@@ -108,32 +108,46 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
     return FARN_OK;
 }
 
-// AUTO rule, from interleaved measurements of both launch shapes (median of 5, on two
-// MI355X boxes; graph replay, cache-hot for calls up to 128 MiB, streaming from HBM above)
-// at 75 points R = 2..8, H = 1024..8192, T = 64..8192, plain and FP8. By vectors per row,
-// nvec = H/8 (the wide shape runs one vector per lane, the narrow shape half as many lanes
-// with two vectors each). Time of the narrow shape against the wide one:
-//   1. nvec in (768, 1024] (H = 6152 .. 8192): narrow, -3 .. -9.5 % (decode -5 .. -9 %,
+// AUTO rule, from interleaved measurements of both launch shapes on MI355X (graph replay,
+// median of 5; cache-hot for calls up to 128 MiB, streaming from HBM above). By vectors per
+// row, nvec = H/8 (the wide shape runs one vector per lane, the narrow shape half as many
+// lanes with two vectors each). Set on about 820 points (R = 2..8, H = 1024..8192,
+// T = 16..8192, plain and FP8: grids over H x T x R and the points of earlier rules, five
+// boxes), its edges adjusted on 320 random points (R = 2..8, H a multiple of 128, T
+// log-uniform over 16..8192; plain, FP8 and MXFP4). Time of the narrow shape against the wide
+// one:
+//   1. nvec in (768, 1024] (H = 6152 .. 8192): narrow, median -3.2 % (decode -5 .. -9 %,
 //      T = 1024 -9 %, T = 8192 -3.3 .. -4.5 %; ties at H = 8192, T = 2048); except the plain
 //      call with nvec > 896 (H > 7168) from T = 4096, where the wide shape is 0.5-2 % faster
 //      at R = 8.
-//   2. nvec in (576, 640] (H = 4616 .. 5120) at 1024 <= T < 2048: narrow, -9 .. -12 % at
-//      R = 8, -2 .. -3 % at R = 2.
-//   3. R <= 4, nvec in (256, 768] (H = 2056 .. 6144) at 512 <= T < 1024 (two ranks: T < 2048):
-//      narrow, up to -22 % (FP8 at T = 512). With few ranks the wide shape keeps only R + 1
-//      loads in flight per lane; the narrow one doubles that. From T = 1024 (four ranks) or
-//      2048 (two) the wide shape is as fast or up to 7 % faster.
-//   4. nvec in (192, 256] (H = 1544 .. 2048) from T = 4096: narrow, -1.5 .. -9 %.
-//   Everything else: wide (the narrow shape up to 7.7 % slower: R = 8, H = 4096 decode).
-// Over the measured points this rule is on average 0.17 % from the faster shape, at most
-// 2.8 % (R = 4, H = 3072, T = 2048, FP8, narrow faster).
+//   2. nvec in (576, 640] (H = 4616 .. 5120) at 768 <= T < 2048: narrow, -3 .. -14 % at
+//      T = 768 .. 1024 (two of 16 points +1.3 and +2.1 %), -2.8 .. +1.5 % at T = 1400 .. 2000.
+//   3. The FP8 call with nvec in (256, 768] (H = 2056 .. 6144) below T = 768, when
+//      nvec <= 464 (H <= 3712) or 256 <= T < 512: narrow, median -5.7 %, down to -21 %, in
+//      five of six points faster; the two-slot kernel overlaps each slot's group reductions and
+//      scale with the other slot's loads. From T = 768 the wide shape is up to 10 % faster at
+//      H = 2560. The MXFP4 call is not in this band: its narrow shape is 3-7 % slower below
+//      T = 100 there.
+//   4. R <= 4, nvec in (256, 768] at 512 <= T < 768 (two ranks: T < 1536): narrow, median
+//      -3.2 %, down to -20 % (FP8, T = 512), up to +10 % at H = 2560. With few ranks the wide shape keeps only R + 1 loads in flight per
+//      lane; the narrow one doubles that. At T = 768 with four ranks the wide shape is 2-10 %
+//      faster; at T = 384 the two are even on average.
+//   Everything else: wide (the narrow shape median 3.9 % slower, up to 36 % at small T and
+//   H <= 2048).
+// Against the faster shape at each point the rule loses 0.48 % on average over the 820 points,
+// 0.50 .. 0.58 % over the 320 random ones, and 0.28 .. 0.46 % (at most 13 .. 16.5 %: R = 3,
+// H = 4608, T = 434, plain) over 160 further random points measured after it was fixed, on two
+// boxes. The previous rule, without
+// band 3 and with a band for H = 1544 .. 2048 from T = 4096 (-1 .. -5 %), lost 1.19 %,
+// 0.95 .. 1.18 % and 1.05 % (at most 19 % on the last set).
 int select(int R, int64_t T, int64_t H, int quant) {
     const int64_t nvec = H / 8;
     if (nvec > 768 && nvec <= 1024)
-        return (!quant && nvec > 896 && T >= 4096) ? FARN_VARIANT_WIDE : FARN_VARIANT_NARROW;
-    if (nvec > 576 && nvec <= 640 && T >= 1024 && T < 2048) return FARN_VARIANT_NARROW;
-    if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 2048 : 1024)) return FARN_VARIANT_NARROW;
-    if (nvec > 192 && nvec <= 256 && T >= 4096) return FARN_VARIANT_NARROW;
+        return (quant == kNone && nvec > 896 && T >= 4096) ? FARN_VARIANT_WIDE : FARN_VARIANT_NARROW;
+    if (nvec > 576 && nvec <= 640 && T >= 768 && T < 2048) return FARN_VARIANT_NARROW;
+    if (quant == kFp8 && nvec > 256 && nvec <= 768 && T < 768 && (nvec <= 464 || (T >= 256 && T < 512)))
+        return FARN_VARIANT_NARROW;
+    if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 1536 : 768)) return FARN_VARIANT_NARROW;
     return FARN_VARIANT_WIDE;
 }
 
@@ -169,7 +183,7 @@ farn_status run(const void *const *partials, int R, const void *residual, const 
     // column-major scales are addressed through one 32-bit buffer range (T and H are in
     // range here, so the product cannot overflow)
     if (cols && T * (H / FARN_GROUP) * 4 >= ((int64_t)1 << 31)) return FARN_ERR_SHAPE;
-    const int shape = variant == FARN_VARIANT_AUTO ? select(R, T, H, quant != kNone ? 1 : 0) : variant;
+    const int shape = variant == FARN_VARIANT_AUTO ? select(R, T, H, quant) : variant;
     farn::Call c;
     for (int r = 0; r < 8; ++r) c.partials[r] = r < R ? partials[r] : nullptr;
     c.R = R;
