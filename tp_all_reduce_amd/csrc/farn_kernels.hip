@@ -488,8 +488,9 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     const rsrc_t r_ro = row_rsrc(k.res_out, ro, rb);
     // Store schedule, chosen by measurement on MI355X. The plain two-slot kernel stores
     // residual_out with out, after the statistics, rather than between the two slots' folds
-    // while slot 1's loads are in flight: 5-8 % faster at decode sizes (H = 7168, 8192) and
-    // ~1 % on the prefill chunk. The one-slot kernels store it as soon as it is folded (1-3 %
+    // while slot 1's loads are in flight: 5-8 % faster at decode sizes (H = 7168, 8192),
+    // 2-14 % at T = 128 .. 2048 (R = 8, H = 7168; at H = 8192 3.6-11 % up to T = 384, within
+    // 0.7 % from T = 512) and ~1 % on the prefill chunk. The one-slot kernels store it as soon as it is folded (1-3 %
     // faster that way). The two-slot quant kernels have two schedules: the streaming one
     // (immediate residual_out, each slot's codes right after its out, FP8 codes
     // non-temporal) for many rows, and kSmall (residual_out after the statistics, FP8: all of
