@@ -30,8 +30,8 @@
 //   narrow - L about NV/2, two vectors per lane: half the waves per row, twice the loads in
 //            flight per lane. On MI355X it is the faster one for H = 6152 .. 8192 (the FP8
 //            prefill call at H = 7168 by 3-4 %, decode by 5-9 %), at H = 4616 .. 5120 for
-//            1024 <= T < 2048, with up to four ranks at mid-size T, and for H <= 2048 from
-//            T = 4096.
+//            768 <= T < 2048, for much of the FP8 call at H = 2056 .. 6144 below T = 768, and
+//            with up to four ranks at mid-size T.
 // The fp64 statistics make the two shapes agree bit for bit in practice (their sums of
 // squares differ only in the order of fp64 additions). The two-slot quant kernels also have
 // two store schedules, one for many rows and one for few (do_row). The host may reserve LDS
