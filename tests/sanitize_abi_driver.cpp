@@ -99,9 +99,10 @@ int main() {
     EXPECT(farn_reduce(parts, 2, 4, 256, A(0, 32), nullptr) == FARN_ERR_ALIAS);
     EXPECT(farn_quant_group(A(12), 4, 256, 128, A(12, 64), (float *)A(15), nullptr) == FARN_ERR_ALIAS);
     EXPECT(g_launches == before);
-    // LDS reserved to hold the streaming FP8 / MXFP4 kernels of long rows (H = 6152 .. 8192,
-    // narrow shape) at two workgroups per compute unit: R >= 6 above 512 rows, R = 4, 5 from
-    // 2048 rows; never for the plain call, the small-call schedule or the wide shape
+    // LDS reserved to hold the narrow kernels of long rows (H = 6152 .. 8192) at two workgroups
+    // per compute unit: FP8 / MXFP4 with R >= 6 above 512 rows and R = 4, 5 from 2048 rows; the
+    // plain call with R = 4 .. 7 from 2048 rows; never for the small-call schedule, the plain
+    // call with R = 8 or R < 4, or the wide shape
     struct LdsCase { int R; int64_t T, H; int quant; int variant; unsigned want; };
     const LdsCase lds_cases[] = {
         {8, 8192, 7168, 1, 0, 56u << 10}, {8, 8192, 7168, 2, 0, 56u << 10}, {8, 8192, 7168, 0, 0, 0},
@@ -109,6 +110,10 @@ int main() {
         {5, 1024, 7168, 1, 0, 0},         {4, 2048, 7168, 1, 0, 56u << 10}, {4, 2047, 7168, 2, 0, 0},
         {2, 8192, 7168, 1, 0, 0},         {8, 8192, 6144, 1, 0, 0},          {8, 8192, 8192, 1, 0, 56u << 10},
         {8, 8192, 7168, 1, FARN_VARIANT_WIDE, 0}, {8, 8192, 8192, 0, FARN_VARIANT_NARROW, 0},
+        {6, 2048, 7168, 0, 0, 56u << 10}, {4, 2048, 6656, 0, 0, 56u << 10}, {4, 2047, 7168, 0, 0, 0},
+        {7, 8192, 7168, 0, 0, 56u << 10}, {3, 8192, 7168, 0, 0, 0},          {6, 4096, 8192, 0, 0, 0},
+        {6, 4096, 8192, 0, FARN_VARIANT_NARROW, 56u << 10}, {6, 2048, 8192, 0, 0, 56u << 10},
+        {7, 8192, 6144, 0, 0, 0},
     };
     for (const LdsCase &lc : lds_cases) {
         farn_status st;

@@ -144,12 +144,12 @@ def test_prefill_full_size_properties(prefill):
     assert ((a[2] & 0x7F) == 0x7E).view(prefill.T, -1, 128).any(dim=2).all()  # a 448 code per group
 
 
-@pytest.mark.parametrize("R,H", [(6, 7168), (8, 6656)])
+@pytest.mark.parametrize("R,H", [(6, 7168), (4, 6656), (7, 8192), (8, 6656)])
 def test_two_workgroups_per_cu_launch(dev, R, H):
-    """The plain call's narrow shape at H = 6152..7168 with R >= 6 and T >= 2048 is launched
-    with LDS reserved so that at most two workgroups share a compute unit: its outputs match the
-    oracle on every row, and the wide shape (launched without the reservation) bit for bit
-    on every row."""
+    """The plain call's narrow shape at H = 6152..8192 with R = 4..7 from T = 2048 is launched
+    with LDS reserved so that at most two workgroups share a compute unit (with R = 8 its
+    registers already allow no more): its outputs match the oracle on every row, and the wide
+    shape (launched without the reservation) bit for bit on every row."""
     T = 2048
     u = Uploaded(make_inputs(CONFIGS["prefill"], seed=40 + R, R=R, T=T, H=H), dev)
     assert F.select_variant(R, T, H, False) == F.VARIANT_NARROW

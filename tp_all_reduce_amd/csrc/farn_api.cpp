@@ -151,22 +151,26 @@ int select(int R, int64_t T, int64_t H, int quant) {
     return FARN_VARIANT_WIDE;
 }
 
-// Workgroups per compute unit of the narrow shape of the FP8 and MXFP4 kernels at nvec in
-// (768, 1024] (7 or 8 waves per row) in the streaming schedule (T > 512): at most two. Their
-// registers (78 VGPRs) allow three, and two stream faster: reserving 56 KiB of LDS per
-// workgroup (of 160 KiB per compute unit), which the kernel does not use, leaves room for two.
-// Measured on MI355X (interleaved, median of 5, H = 7168), against no reservation: R = 8:
-// T = 1024 -1.4 %, T = 2048 -4.0 %, T = 8192 -2.7 .. -3.1 %; R = 6: -1.4 .. -3.8 %; R = 5 and
-// 4 from T = 2048: -1.0 .. -3.5 %, but +0.6 .. +5.9 % at T = 1024. The plain kernels and the
-// small-call schedule hold 86-91 VGPRs, so two is already their limit (a reservation there
-// measured 0 .. +1.3 %).
+// Workgroups per compute unit of the narrow shape at nvec in (768, 1024] (7 or 8 waves per
+// row) in calls of many rows: at most two. Registers allow three for the streaming FP8 and
+// MXFP4 kernels (78-79 VGPRs) and for the plain kernel with up to seven ranks (80; with eight,
+// 91 VGPRs hold it at two), and two stream faster: reserving 56 KiB of LDS per workgroup (of
+// 160 KiB per compute unit), which the kernel does not use, leaves room for two.
+// Measured on MI355X (interleaved, median of 5, H = 7168 unless stated), against no
+// reservation: FP8 and MXFP4, R = 8: T = 1024 -1.4 %, T = 2048 -4.0 %, T = 8192 -2.7 .. -3.1 %;
+// R = 6: -1.4 .. -3.8 %; R = 5 and 4 from T = 2048: -1.0 .. -3.5 %, but +0.6 .. +5.9 % at
+// T = 1024. Plain, R = 4..7 from T = 2048: -0.9 .. -3.2 % at H = 6656 and 7168 (up to +1.8 %
+// at H = 8192, where the wide shape runs the plain call from T = 4096); at T = 1024 +0.4 ..
+// +4.7 %, and with two ranks +1.4 .. +3.5 % from T = 2048. The small-call schedule (T <= 512)
+// holds 82-83 VGPRs, so two is already its limit.
 constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
 
 unsigned lds_reserve(int R, int64_t T, int64_t H, Quant quant, int shape) {
     const int64_t nvec = H / 8;
-    const bool long_row_narrow = shape == FARN_VARIANT_NARROW && nvec > 768 && nvec <= 1024;
-    const bool streaming = T > farn::kSmallCallRows;
-    return (quant != kNone && long_row_narrow && streaming && (R >= 6 || (R >= 4 && T >= 2048))) ? kLdsTwoPerCu : 0u;
+    if (shape != FARN_VARIANT_NARROW || nvec <= 768 || nvec > 1024) return 0u;
+    if (quant != kNone)
+        return (T > farn::kSmallCallRows && (R >= 6 || (R >= 4 && T >= 2048))) ? kLdsTwoPerCu : 0u;
+    return (R >= 4 && R <= 7 && T >= 2048) ? kLdsTwoPerCu : 0u;
 }
 
 farn_status run(const void *const *partials, int R, const void *residual, const void *gamma,

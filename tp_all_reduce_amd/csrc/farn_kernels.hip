@@ -19,7 +19,8 @@
 //   in fp32 in rank order, the residual added last, the sum rounded to bf16
 //   (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
-//   per wave through LDS -> every wave adds the per-wave values in wave order; the
+//   per wave through LDS -> each lane reads one wave's value and a 16-lane butterfly
+//   adds them (the same fixed order in every wave); the
 //   normalisation product is rounded once to bf16 (formed in fp32 where that provably
 //   gives the same value, else in fp64). The row never passes through LDS; only one
 //   double per wave does.
@@ -74,6 +75,7 @@ struct Params {
 };
 
 constexpr int kMaxWaves = 16;
+static_assert(kMaxWaves == 16, "the per-wave values are read by one 16-lane DPP row");
 
 // Output quant modes of the fused kernel.
 constexpr int kQuantNone = 0;   // bf16 out only
@@ -212,12 +214,14 @@ __device__ __forceinline__ uint32_t row16_umax(uint32_t x) {
     return x;
 }
 
-// fp64 through DPP: the two 32-bit halves move with the same control.
+// fp64 through DPP: the two 32-bit halves move with the same control. Every control used
+// here reads a lane inside the same 16-lane row, so all lanes are written and no previous
+// value of the destination is needed (bound_ctrl set, full masks).
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double x) {
     const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = dpp_u<CTRL>((uint32_t)u);
-    const uint32_t hi = dpp_u<CTRL>((uint32_t)(u >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
@@ -306,8 +310,10 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
 }
 
 // Row statistics in fp64: wave DPP tree, one double per wave through `slot` (kMaxWaves
-// doubles), one barrier, then every wave adds the per-wave values in wave order; then
-// rstd = 1/sqrt(m) for m = ss/H + eps. fp64 statistics put `out` on the bf16 value the
+// doubles; wave 0 sets the slots past the row's waves to zero), one barrier, then lane l of
+// every wave reads slot l mod 16 and the 16-lane DPP butterfly adds them, in one fixed order
+// for every wave and lane (one LDS read after the barrier rather than one per wave, read one
+// after another: 1-5 % off a decode call); then rstd = 1/sqrt(m) for m = ss/H + eps. fp64 statistics put `out` on the bf16 value the
 // exact statistics give (an fp32 tree moves about one element in 10^4 by one bf16 step,
 // and when that element is a group's amax its scale moves by up to 2^-7); MI355X runs
 // fp64 vector FMAs at the rate of unpacked fp32 ones.
@@ -324,9 +330,9 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     const int nwaves = (int)blockDim.x >> 6;
     const double wsum = wave_sum_d(ss);
     if (lane == 0) slot[wave] = wsum;
+    if (wave == 0 && lane >= nwaves && lane < kMaxWaves) slot[lane] = 0.0;
     __syncthreads();
-    double tot = 0.0;
-    for (int i = 0; i < nwaves; ++i) tot = tot + slot[i];
+    const double tot = row16_sum_d(slot[lane & (kMaxWaves - 1)]);
     const double m = __builtin_fma(tot, k.inv_h, (double)k.eps);
     double r;
     if (m >= 0x1p-1000 && m <= 0x1p1000) {  // the same in every lane of the row
