@@ -159,9 +159,9 @@ int select(int R, int64_t T, int64_t H, int quant) {
 // Measured on MI355X (interleaved, median of 5, H = 7168 unless stated), against no
 // reservation: FP8 and MXFP4, R = 8: T = 1024 -1.4 %, T = 2048 -4.0 %, T = 8192 -2.7 .. -3.1 %;
 // R = 6: -1.4 .. -3.8 %; R = 5 and 4 from T = 2048: -1.0 .. -3.5 %, but +0.6 .. +5.9 % at
-// T = 1024. Plain, R = 4..7 from T = 2048: -0.9 .. -3.2 % at H = 6656 and 7168 (up to +1.8 %
-// at H = 8192, where the wide shape runs the plain call from T = 4096); at T = 1024 +0.4 ..
-// +4.7 %, and with two ranks +1.4 .. +3.5 % from T = 2048. The small-call schedule (T <= 512)
+// T = 1024. Plain, R = 4..7 from T = 2048: -0.9 .. -3.3 % at H = 6656 and 7168 (-2.9 ..
+// +1.8 % at H = 8192, where the wide shape runs the plain call from T = 4096); at T = 1024
+// 0 .. +4.7 %, and with two ranks +0.2 .. +3.5 % from T = 2048. The small-call schedule (T <= 512)
 // holds 82-83 VGPRs, so two is already its limit.
 constexpr unsigned kLdsTwoPerCu = 56u * 1024u;
 
