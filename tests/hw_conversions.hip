@@ -1,8 +1,9 @@
 /*
  * Test kernels for the GPU conversion instructions the FP8 and MXFP4 paths rely on
  * (tests/test_gpu_conversions.py): v_cvt_pk_fp8_f32 over a range of fp32 bit patterns,
- * v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent, and the
- * fused kernels' reciprocal square root (v_rsq_f64 and two Newton steps).
+ * v_cvt_scalef32_pk_fp4_f32 over a list of values under every E8M0 block exponent, the
+ * fused kernels' reciprocal square root (v_rsq_f64 and two Newton steps), and their FP8 group
+ * scale and its reciprocal (an FMA-corrected product by 1/448; v_rcp_f32 and one Newton step).
  * Built by tp_all_reduce_amd/build.py; not part of the library.
  */
 #include <hip/hip_runtime.h>
@@ -41,6 +42,36 @@ __global__ void rsq_newton(const double *m, double *out, uint32_t n) {
     const double y1 = __builtin_fma(y0, __builtin_fma(-hm * y0, y0, 0.5), y0);
     out[2 * i] = y0;
     out[2 * i + 1] = __builtin_fma(y1, __builtin_fma(-hm * y1, y1, 0.5), y1);
+}
+
+// For amax = the fp32 whose bits are amax_bits[i] (a bf16 magnitude pattern shifted left 16):
+// out[3i] = scale = amax/448 and out[3i+1] = 1/(scale * k) as the FP8 quant forms them, with k =
+// 2^64 for scale < 2^-64 (else 1); out[3i+2] = scale * k. The same sequence as quant_slots in
+// the library's kernel source.
+__global__ void fp8_scale_inv(const uint32_t *amax_bits, float *out, uint32_t n) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t amax = amax_bits[i];
+    const float c = 0x1.24924ap-9f;
+    const float a = __uint_as_float(amax);
+    const float q0 = a * c;
+    const float r = __builtin_fmaf(-q0, 448.0f, a);
+    const float scale = amax < 0x7f800000u ? __builtin_fmaf(r, c, q0) : q0;
+    const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
+    const float sk = scale * k;
+    const float y = __builtin_amdgcn_rcpf(sk);
+    const float yn = __builtin_fmaf(__builtin_fmaf(-sk, y, 1.0f), y, y);
+    out[3 * i] = scale;
+    out[3 * i + 1] = scale == 0.0f ? 0.0f : (__builtin_isfinite(sk) ? yn : y);
+    out[3 * i + 2] = sk;
+}
+
+extern "C" int hwconv_fp8_scale_inv(const void *amax_bits, void *out, uint32_t n, void *stream) {
+    if (n == 0 || n > (1u << 20)) return 1;
+    const uint32_t block = 256, grid = (n + block - 1) / block;
+    hipLaunchKernelGGL(fp8_scale_inv, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const uint32_t *)amax_bits,
+                       (float *)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 extern "C" int hwconv_rsq_newton(const void *m, void *out, uint32_t n, void *stream) {

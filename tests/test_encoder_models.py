@@ -1,14 +1,14 @@
 """Exhaustive CPU check of the arithmetic the FP8 kernel does before its conversion
 instruction: the binary32 quotient o / scale computed without a divide (`fp32_quotient` in
 tp_all_reduce_amd/csrc/farn_kernels.hip: q0 = o*inv, the negated remainder nr = q0*scale - o by
-FMA, q0 - nr*inv by FMA; with `quant_slot`'s per-group scale, 2^64 rescaling of tiny groups and clamped remainder
+FMA, q0 - nr*inv by FMA; with `quant_slots`' per-group scale, 2^64 rescaling of tiny groups and clamped remainder
 scale). That quotient can differ from the correctly rounded one by an fp32 unit; this test
 shows that its round-to-nearest-even E4M3 code never does, for every finite bf16 value each
 group can hold, over ~3,300 group maxima (every bf16 subnormal amax included), signed zeros
 included (a -0 value keeps the -0 code 0x80 the division gives). The conversion
 instruction's own rounding is checked on the GPU (tests/test_gpu_conversions.py); here it is
 the oracle's E4M3 encoder. A model is only as faithful as its transcription: a change to
-`fp32_quotient` or to `quant_slot`'s per-group arithmetic must be repeated here.
+`fp32_quotient` or to `quant_slots`' per-group arithmetic must be repeated here.
 
 fp32 steps map one to one onto numpy float32 operations (round to nearest even, subnormals
 kept); fp32 FMAs are modelled exactly (`_fma32`). The reference is the oracle's encoder of the
@@ -55,8 +55,11 @@ def quotient_model(o: np.ndarray, scale_r: np.float32, inv: np.float32) -> np.nd
 
 
 def group_codes_model(o: np.ndarray, amax: np.float32) -> tuple[np.ndarray, np.float32]:
-    """Model of `quant_slot`'s per-group arithmetic for a group with max magnitude amax:
-    scale = amax/448 correctly rounded, the 2^64 rescaling of tiny groups, inv = 1/scale, the
+    """Model of `quant_slots`' per-group arithmetic for a group with max magnitude amax:
+    scale = amax/448 correctly rounded, the 2^64 rescaling of tiny groups, inv = 1/scale (the
+    kernel's FMA-corrected scale and Newton-refined reciprocal equal these two divisions for
+    every bf16 amax: test_fast_scale_is_the_division here, and on the GPU
+    tests/test_gpu_conversions.py), the
     remainder's scale clamped to the largest finite float; codes are the round-to-nearest-even
     E4M3 codes of the quotients (the conversion instruction; here the oracle's encoder)."""
     scale = F32(np.float64(amax) / 448.0)  # amax/448 is never a tie in fp32, so one rounding
@@ -230,3 +233,39 @@ def test_norm_fast_path_equals_one_rounding():
         same = (got == want) | (((got & 0x7FFF) > 0x7F80) & ((want & 0x7FFF) > 0x7F80))
         assert same.all(), (rstd, yy.ravel()[~same][:4], gg.ravel()[~same][:4])
     assert checked > 2_000_000
+
+
+def fast_scale_model(amax: np.ndarray) -> np.ndarray:
+    """Model of the kernel's scale for finite amax: q0 = amax * RN(1/448), then
+    q0 + (amax - q0 * 448) * RN(1/448) by two FMAs (`quant_slots`)."""
+    c = F32(1.0) / F32(448.0)
+    a = np.asarray(amax, np.float32)
+    q0 = (a * c).astype(np.float32)
+    r = _fma32(-q0, np.full_like(q0, 448.0), a)
+    return _fma32(r, np.full_like(q0, c), q0)
+
+
+def test_fast_scale_is_the_division():
+    """For every finite non-negative bf16 amax (zero and subnormals included) the FMA-corrected
+    product equals the correctly rounded amax/448; also in exact rationals on a sample."""
+    amax = ALL_BF16[:0x7F80]  # the magnitude patterns 0x0000 .. 0x7F7F: every finite amax
+    assert np.isfinite(amax).all() and amax.size == 32640
+    got = fast_scale_model(amax)
+    want = (amax / F32(448.0)).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    c = Fraction(float(F32(1.0) / F32(448.0)))
+    for a in amax[:: 97]:
+        exact = Fraction(float(a)) / 448
+        g = Fraction(float(fast_scale_model(np.array([a]))[0]))
+        w = float(want[amax == a][0])
+        assert g == Fraction(w) and abs(g - exact) <= abs(Fraction(float(np.nextafter(F32(w), F32(np.inf)))) - exact)
+    assert c == Fraction(float.fromhex("0x1.24924ap-9"))
+
+
+def test_uncorrected_scale_would_fail():
+    """The product alone (no FMA correction) is not the division for some group maxima, so the
+    previous test can tell the two apart."""
+    amax = ALL_BF16[:0x7F80]
+    q0 = (amax * (F32(1.0) / F32(448.0))).astype(np.float32)
+    want = (amax / F32(448.0)).astype(np.float32)
+    assert np.count_nonzero(q0.view(np.uint32) != want.view(np.uint32)) > 0

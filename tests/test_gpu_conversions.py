@@ -41,6 +41,7 @@ def hw():
     L.hwconv_fp8_of_bits.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
     L.hwconv_fp4_all_scales.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
     L.hwconv_rsq_newton.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    L.hwconv_fp8_scale_inv.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
     return L
 
 
@@ -117,3 +118,33 @@ def test_rsq_newton_within_two_units(hw):
         lo_n, hi_n = np.nextafter(lo, -np.inf), np.nextafter(hi, np.inf)
         x = Fraction(float(m[i]))
         assert Fraction(float(lo_n)) ** 2 * x < 1 < Fraction(float(hi_n)) ** 2 * x, (m[i], got[i])
+
+
+def test_fp8_scale_and_reciprocal_exact(hw):
+    """The FP8 quant's group scale and its reciprocal, for every 16-bit magnitude pattern a bf16
+    group maximum can have (zero, subnormals, normals, inf, every NaN): the FMA-corrected product
+    by RN(1/448) equals the IEEE single division amax / 448 bit for bit (a NaN gives a NaN), and
+    v_rcp_f32 refined by one Newton step equals the IEEE single division 1 / (scale * k) (k = 2^64
+    below 2^-64, else 1; 0 for a zero scale), so the quotients of the quant are those whose codes
+    the CPU model checks for every group maximum."""
+    bits = (np.arange(0x8000, dtype=np.uint32) << 16)
+    dbits = torch.from_numpy(bits.view(np.int32)).to("cuda")
+    out = torch.empty(3 * bits.size, dtype=torch.float32, device="cuda")
+    say(f"[gpu] FP8 scale and reciprocal over {bits.size} magnitude patterns")
+    assert hw.hwconv_fp8_scale_inv(dbits.data_ptr(), out.data_ptr(), bits.size, _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, 3)
+    amax = bits.view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        scale = amax / np.float32(448.0)
+        k = np.where(scale < np.float32(2.0 ** -64), np.float32(2.0 ** 64), np.float32(1.0)).astype(np.float32)
+        sk = (scale * k).astype(np.float32)
+        inv = np.where(scale == 0, np.float32(0.0), np.float32(1.0) / sk).astype(np.float32)
+    nan = np.isnan(scale)
+    assert np.array_equal(np.isnan(got[:, 0]), nan)
+    assert np.array_equal(got[~nan, 0].view(np.uint32), scale[~nan].view(np.uint32)), \
+        amax[~nan][np.nonzero(got[~nan, 0].view(np.uint32) != scale[~nan].view(np.uint32))[0][:5]]
+    assert np.array_equal(got[~nan, 2].view(np.uint32), sk[~nan].view(np.uint32))
+    assert np.array_equal(np.isnan(got[:, 1]), nan)
+    bad = np.nonzero(got[~nan, 1].view(np.uint32) != inv[~nan].view(np.uint32))[0]
+    assert bad.size == 0, [(float(amax[~nan][i]), float(got[~nan, 1][i]), float(inv[~nan][i])) for i in bad[:5]]

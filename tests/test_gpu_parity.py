@@ -515,6 +515,38 @@ def test_quant_alone_shapes(dev, H):
 
 
 
+def test_quant_every_group_max(dev):
+    """One 128-channel group for each of the 32,768 bf16 magnitude patterns as its maximum (zero,
+    subnormals, normals, inf, every NaN), its other channels random below it with random signs:
+    the quant alone gives scales bit-identical to the oracle's (IEEE single divisions) for every
+    one of them, and codes bit-identical wherever the quotient is a number. A NaN group's
+    quotients are NaN, whose sign IEEE 754 leaves open (the oracle's division keeps the NaN
+    operand's sign, the kernel's correction step may flip it): there both codes must be NaN
+    codes (0x7F / 0xFF)."""
+    rng = np.random.default_rng(91)
+    T, H = 512, 8192
+    ng = H // 128
+    p = np.arange(0x8000, dtype=np.uint32).reshape(T, ng)
+    mag = rng.integers(0, 1 << 16, size=(T, ng, 128), dtype=np.uint32) % (p[..., None] + 1)
+    mag[np.arange(T)[:, None], np.arange(ng)[None, :], rng.integers(0, 128, size=(T, ng))] = p
+    sign = rng.integers(0, 2, size=mag.shape, dtype=np.uint32) << 15
+    xb = (mag | sign).astype(np.uint16).reshape(T, H)
+    say(f"[gpu] quant alone, every group maximum T={T} H={H}")
+    q, s = F.quant_group(to_dev_bf16(xb, dev))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_group(xb)
+    gs, gq = s.cpu().numpy(), q.cpu().numpy()
+    nan = np.isnan(rs)
+    assert nan.sum() == 0x8000 - 0x7F81 and np.array_equal(np.isnan(gs), nan)
+    assert np.array_equal(gs[~nan].view(np.uint32), rs[~nan].view(np.uint32))
+    ref_nan = (rq & 0x7F) == 0x7F  # every code of a NaN group, and inf / inf in the inf group
+    assert ref_nan[np.repeat(nan, 128, axis=1)].all()
+    bad = np.nonzero((gq != rq) & ~ref_nan)
+    assert bad[0].size == 0, [(int(p[r, c // 128]), int(xb[r, c]), int(gq[r, c]), int(rq[r, c]))
+                              for r, c in zip(*(b[:5] for b in bad))]
+    assert ((gq[ref_nan] & 0x7F) == 0x7F).all()
+
+
 # ------------------------------------------------------------------ MXFP4 output
 def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label="", ref=None):
     say(f"[gpu] mxfp4 {label} R={u.R} T={u.T} H={u.H} variant={variant} emit={emit_out}")

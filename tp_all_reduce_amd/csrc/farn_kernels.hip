@@ -204,16 +204,6 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-// Max of non-negative float bit patterns as unsigned integers: orders every finite
-// value and inf, and a NaN (above inf) wins, so NaN propagates into the scale.
-__device__ __forceinline__ uint32_t row16_umax(uint32_t x) {
-    x = max(x, dpp_u<0xB1>(x));
-    x = max(x, dpp_u<0x4E>(x));
-    x = max(x, dpp_u<0x141>(x));
-    x = max(x, dpp_u<0x140>(x));
-    return x;
-}
-
 // fp64 through DPP: the two 32-bit halves move with the same control. Every control used
 // here reads a lane inside the same 16-lane row, so all lanes are written and no previous
 // value of the destination is needed (bound_ctrl set, full masks).
@@ -347,8 +337,17 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     return r;
 }
 
-// E4M3 codes of one vector slot (8 bf16 values, two per word of `ob`) and, from one lane
-// per 16-lane group, the group's scale, stored at byte sbase + group * sstride of r_sc.
+// RN(1/448): the scale amax/448 is formed as q0 = amax * c corrected by one FMA of the
+// remainder, q0 + (amax - q0 * 448) * c. Over every finite bf16 amax (32,640 values, zero and
+// subnormals included) this equals the correctly rounded quotient (checked in exact rational
+// arithmetic, tests/test_encoder_models.py, and on the GPU for every 16-bit magnitude
+// pattern, tests/test_gpu_conversions.py); inf and NaN take q0 (inf, or the quieted NaN).
+constexpr float kInv448 = 0x1.24924ap-9f;
+
+// E4M3 codes of N vector slots (8 bf16 values each, two per word of `ob`) and, from one lane
+// per 16-lane group, each group's scale, stored at byte sbase + group * sstride of r_sc. The
+// slots' steps are written side by side, so their dependent chains (group max, scale,
+// reciprocal) overlap.
 // The group's amax is a packed 16-bit max of the magnitude patterns (bf16 magnitudes
 // order as unsigned integers, inf included, and a NaN, above inf, wins and propagates
 // into the scale). Each code is the conversion of the binary32 quotient o / scale, sign
@@ -358,39 +357,75 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
 // its lanes on the arithmetic path (their quotients are +-0) and a mask clears the signs.
 // A group whose scale is below 2^-64 is quantised from o and scale both times 2^64 (exact;
 // the quotient is the same), so that 1/scale and the remainder stay normal numbers; the
-// stored scale is the unscaled one.
+// stored scale is the unscaled one. 1/scale is the hardware reciprocal refined by one Newton
+// step (y + y * (1 - s * y)), which equals the correctly rounded reciprocal for every scale
+// a bf16 amax can produce (checked on the GPU for all of them); 1/inf = 0 and NaN come from
+// the hardware reciprocal itself.
+template <int P, int N>
+__device__ __forceinline__ void quant_slots(const u32x4 (&ob)[N], rsrc_t r_q, rsrc_t r_sc, const uint32_t (&off)[N],
+                                            uint32_t sbase, uint32_t sstride) {
+    uint32_t amax[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        u16x2 m = u16x2{0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[n][w] & 0x7fff7fffu));
+        amax[n] = max((uint32_t)m[0], (uint32_t)m[1]);
+    }
+    // 16 lanes = one 128-channel group: a DPP butterfly of unsigned maxima (the magnitude
+    // patterns of non-negative floats order as integers), slot by slot
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0xB1>(amax[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0x4E>(amax[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0x141>(amax[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0x140>(amax[n])) << 16;
+    float scale[N], k[N], inv[N], sr[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float a = __uint_as_float(amax[n]);
+        const float q0 = a * kInv448;
+        const float r = __builtin_fmaf(-q0, 448.0f, a);
+        scale[n] = amax[n] < 0x7f800000u ? __builtin_fmaf(r, kInv448, q0) : q0;
+        k[n] = scale[n] < 0x1p-64f ? 0x1p64f : 1.0f;
+        const float sk = scale[n] * k[n];
+        const float y = __builtin_amdgcn_rcpf(sk);
+        const float yn = __builtin_fmaf(__builtin_fmaf(-sk, y, 1.0f), y, y);
+        inv[n] = scale[n] == 0.0f ? 0.0f : (__builtin_isfinite(sk) ? yn : y);
+        sr[n] = min(sk, 0x1.fffffep127f);
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        float v[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = fp32_quotient(bf_lo(ob[n][w]) * k[n], sr[n], inv[n]);
+            v[2 * w + 1] = fp32_quotient(bf_hi(ob[n][w]) * k[n], sr[n], inv[n]);
+        }
+        const uint32_t keep = scale[n] == 0.0f ? 0u : 0xffffffffu;
+        u32x2 codes;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d], v[4 * d + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2], v[4 * d + 3], word, true);
+            codes[d] = (uint32_t)word & keep;
+        }
+        st8<P>(codes, r_q, off[n] >> 1);
+        // one lane per group writes the scale; the others aim past the row (dropped)
+        const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off[n] >> 8) * sstride : kDropOffset;
+        st4<P>(scale[n], r_sc, soff);
+    }
+}
+
 template <int P>
 __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, uint32_t off, uint32_t sbase,
                                            uint32_t sstride) {
-    u16x2 m = u16x2{0, 0};
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[w] & 0x7fff7fffu));
-    // 16 lanes = one 128-channel group
-    const uint32_t amax = row16_umax(max((uint32_t)m[0], (uint32_t)m[1])) << 16;
-    const float scale = __uint_as_float(amax) / 448.0f;  // correctly rounded
-    const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
-    const float sk = scale * k;
-    const float inv = scale == 0.0f ? 0.0f : 1.0f / sk;
-    const float sr = min(sk, 0x1.fffffep127f);
-    float v[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        v[2 * w] = fp32_quotient(bf_lo(ob[w]) * k, sr, inv);
-        v[2 * w + 1] = fp32_quotient(bf_hi(ob[w]) * k, sr, inv);
-    }
-    const uint32_t keep = scale == 0.0f ? 0u : 0xffffffffu;
-    u32x2 codes;
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d], v[4 * d + 1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * d + 2], v[4 * d + 3], word, true);
-        codes[d] = (uint32_t)word & keep;
-    }
-    st8<P>(codes, r_q, off >> 1);
-    // one lane per group writes the scale; the others aim past the row (dropped)
-    const uint32_t soff = ((int)threadIdx.x & 15) == 0 ? sbase + (off >> 8) * sstride : kDropOffset;
-    st4<P>(scale, r_sc, soff);
+    const u32x4 obs[1] = {ob};
+    const uint32_t offs[1] = {off};
+    quant_slots<P, 1>(obs, r_q, r_sc, offs, sbase, sstride);
 }
 
 // MXFP4 of one vector slot: the 32-channel block spans the 4 lanes of a quad. Shared
@@ -543,8 +578,10 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
             st16(yb[v], r_ro, off0 + v * L16);
             ob[v] = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
         }
+        uint32_t offs[VPL];
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) quant_slot<kCodeP>(ob[v], r_q, r_sc, off0 + v * L16, sbase, sstride);
+        for (int v = 0; v < VPL; ++v) offs[v] = off0 + v * L16;
+        quant_slots<kCodeP, VPL>(ob, r_q, r_sc, offs, sbase, sstride);
     } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
