@@ -303,10 +303,10 @@ __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &
 // doubles; wave 0 sets the slots past the row's waves to zero), one barrier, then lane l of
 // every wave reads slot l mod 16 and the 16-lane DPP butterfly adds them, in one fixed order
 // for every wave and lane (one LDS read after the barrier rather than one per wave, read one
-// after another: 1-5 % off a decode call); then rstd = 1/sqrt(m) for m = ss/H + eps. fp64 statistics put `out` on the bf16 value the
-// exact statistics give (an fp32 tree moves about one element in 10^4 by one bf16 step,
-// and when that element is a group's amax its scale moves by up to 2^-7); MI355X runs
-// fp64 vector FMAs at the rate of unpacked fp32 ones.
+// after another: 1-5 % off a decode call); then rstd = 1/sqrt(m) for m = ss/H + eps. fp64
+// statistics put `out` on the bf16 value the exact statistics give (an fp32 tree moves about
+// one element in 10^4 by one bf16 step, and when that element is a group's amax its scale
+// moves by up to 2^-7); MI355X runs fp64 vector FMAs at the rate of unpacked fp32 ones.
 // m is formed as ss * (1/H) + eps by one FMA, and 1/sqrt(m) as the hardware reciprocal
 // square root (about 24 correct bits, measured) refined by two Newton steps
 // (y += y * (1/2 - m y^2 / 2)): the result sits within two fp64 units of the correctly
@@ -531,8 +531,8 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     // residual_out with out, after the statistics, rather than between the two slots' folds
     // while slot 1's loads are in flight: 5-8 % faster at decode sizes (H = 7168, 8192),
     // 2-14 % at T = 128 .. 2048 (R = 8, H = 7168; at H = 8192 3.6-11 % up to T = 384, within
-    // 0.7 % from T = 512) and ~1 % on the prefill chunk. The one-slot kernels store it as soon as it is folded (1-3 %
-    // faster that way). The two-slot quant kernels have two schedules: the streaming one
+    // 0.7 % from T = 512) and ~1 % on the prefill chunk. The one-slot kernels store it as soon
+    // as it is folded (1-3 % faster that way). The two-slot quant kernels have two schedules: the streaming one
     // (immediate residual_out, each slot's codes right after its out, FP8 codes
     // non-temporal) for many rows, and kSmall (residual_out after the statistics, FP8: all of
     // out before the codes, codes and scales sc1) for few rows, where it is 4-15 % faster
