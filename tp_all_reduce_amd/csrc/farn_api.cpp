@@ -129,9 +129,9 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //      H = 2560. The MXFP4 call is not in this band: its narrow shape is 3-7 % slower below
 //      T = 100 there.
 //   4. R <= 4, nvec in (256, 768] at 512 <= T < 768 (two ranks: T < 1536): narrow, median
-//      -3.2 %, down to -20 % (FP8, T = 512), up to +10 % at H = 2560. With few ranks the wide shape keeps only R + 1 loads in flight per
-//      lane; the narrow one doubles that. At T = 768 with four ranks the wide shape is 2-10 %
-//      faster; at T = 384 the two are even on average.
+//      -3.2 %, down to -20 % (FP8, T = 512), up to +10 % at H = 2560. With few ranks the wide
+//      shape keeps only R + 1 loads in flight per lane; the narrow one doubles that. At T = 768
+//      with four ranks the wide shape is 2-10 % faster; at T = 384 the two are even on average.
 //   Everything else: wide (the narrow shape median 3.9 % slower, up to 36 % at small T and
 //   H <= 2048).
 // Against the faster shape at each point the rule loses 0.48 % on average over the 820 points,
