@@ -451,9 +451,10 @@ def shape_points(n, seed):
     return pts
 
 
-def shapes_check(dev, n, seed):
+def shapes_check(dev, n, seed, cold=False):
     """Both launch shapes forced at n random call shapes (graph replay, interleaved, median of
-    5; cache-hot for calls up to 128 MiB, buffer sets rotated over >= 1 GiB above), and what the
+    5; cache-hot for calls up to 128 MiB, buffer sets rotated over >= 1 GiB above, or rotated
+    at every size with cold=True, as when each call's inputs stream from HBM), and what the
     automatic rule loses at each against the faster of the two."""
     points = []
     for (R, H, T, quant) in shape_points(n, seed):
@@ -461,7 +462,7 @@ def shapes_check(dev, n, seed):
         b = Bufs(make_inputs(cfg, seed=R * 1000 + T + H), dev, quant, True)
         nb = nbytes(cfg, quant, True)
         us_est = max(3.0, nb / 6.0e12 * 1e6)
-        if nb <= (128 << 20):
+        if nb <= (128 << 20) and not cold:
             sets, calls, replays = [b], max(10, min(200, int(8000 / us_est))), 5
         else:
             k = max(1, -(-(1 << 30) // nb))
@@ -484,6 +485,7 @@ def shapes_check(dev, n, seed):
     losses = sorted((p["auto_loss_pct"] for p in points), reverse=True)
     return {"what": "both launch shapes at random call shapes; auto_loss_pct = the automatic rule's "
                     "time over the faster shape's, in per cent",
+            "inputs": "streaming from HBM at every size" if cold else "cache-hot up to 128 MiB, streaming above",
             "seed": seed, "points": len(points), "auto_loss_mean_pct": round(statistics.mean(losses), 3),
             "auto_loss_max_pct": losses[0], "points_over_5pct": sum(1 for x in losses if x > 5),
             "always_wide_loss_mean_pct": round(statistics.mean(
@@ -539,6 +541,8 @@ def main():
                     help="instead of the bench: time both launch shapes at N random call shapes and "
                          "report what the automatic rule loses against the faster one (one JSON line)")
     ap.add_argument("--shapes-seed", type=int, default=13)
+    ap.add_argument("--shapes-cold", action="store_true",
+                    help="with --shapes: time every call with its inputs streaming from HBM")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one torch copy of 1 GiB (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -552,7 +556,8 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     if args.shapes > 0:
-        print(json.dumps({"shapes_check": shapes_check(dev, args.shapes, args.shapes_seed)}), flush=True)
+        print(json.dumps({"shapes_check": shapes_check(dev, args.shapes, args.shapes_seed, args.shapes_cold)}),
+              flush=True)
         return
     cfg, quant, emit_out = WORKLOADS[args.workload]
     variant = VARIANT_NAMES[args.variant]
