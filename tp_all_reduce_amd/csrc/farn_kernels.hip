@@ -230,13 +230,6 @@ __device__ __forceinline__ double readlane_d(double x, int lane) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Max over the 4 lanes of a quad (one 32-channel MXFP4 block: 4 lanes x 8 values).
-__device__ __forceinline__ uint32_t quad_umax(uint32_t x) {
-    x = max(x, dpp_u<0xB1>(x));
-    x = max(x, dpp_u<0x4E>(x));
-    return x;
-}
-
 // Wave total: the four 16-lane row totals, read as scalars and added in a fixed order.
 __device__ __forceinline__ double wave_sum_d(double x) {
     x = row16_sum_d(x);
@@ -428,32 +421,49 @@ __device__ __forceinline__ void quant_slot(u32x4 ob, rsrc_t r_q, rsrc_t r_sc, ui
     quant_slots<P, 1>(obs, r_q, r_sc, offs, sbase, sstride);
 }
 
-// MXFP4 of one vector slot: the 32-channel block spans the 4 lanes of a quad. Shared
-// scale 2^s with s = floor(log2 amax) - 2 (E2M1's largest exponent), clamped to the
-// E8M0 range; a block holding a NaN gets the NaN scale 0xFF and zero codes, an all-zero
-// block scale 2^-127 (byte 0) and zero codes. The conversion takes the scale as an fp32
-// whose exponent field is the E8M0 byte (s = -127 is the bit pattern 0), scales each value
-// by 2^-s exactly and rounds it to E2M1; element 2i goes to the low nibble of its byte.
-__device__ __forceinline__ void mxfp4_slot(const float (&o)[8], rsrc_t r_q, rsrc_t r_sc, uint32_t off) {
-    uint32_t amax = 0u;
+// MXFP4 of N vector slots from their packed bf16 values, the slots' steps written side by
+// side: the 32-channel block spans the 4 lanes of a quad. Shared scale 2^s with
+// s = floor(log2 amax) - 2 (E2M1's largest exponent), clamped to the E8M0 range; a block
+// holding a NaN gets the NaN scale 0xFF and zero codes, an all-zero block scale 2^-127
+// (byte 0) and zero codes. The block max is a packed 16-bit max of the bf16 magnitude
+// patterns (they order as integers, and a NaN, above inf, wins), then two DPP steps. The
+// conversion takes the scale as an fp32 whose exponent field is the E8M0 byte (s = -127 is
+// the bit pattern 0), scales each value by 2^-s exactly and rounds it to E2M1; element 2i goes
+// to the low nibble of its byte.
+template <int N>
+__device__ __forceinline__ void mxfp4_slots(const u32x4 (&ob)[N], rsrc_t r_q, rsrc_t r_sc,
+                                            const uint32_t (&off)[N]) {
+    uint32_t amax[N];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = max(amax, __float_as_uint(o[e]) & 0x7fffffffu);
-    amax = quad_umax(amax);
-    const bool nan_blk = amax > 0x7f800000u;
-    const bool zero_blk = amax == 0u;
-    int sexp = __builtin_amdgcn_frexp_expf(__uint_as_float(amax)) - 1 - 2;  // floor(log2 amax) - 2
-    sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
-    const float sc = __uint_as_float((uint32_t)(sexp + 127) << 23);
-    uint32_t word = 0u;
-    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[0], o[1], sc, 0);
-    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[2], o[3], sc, 1);
-    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[4], o[5], sc, 2);
-    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, o[6], o[7], sc, 3);
-    const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
-    st4_mx(word & keep, r_q, off >> 2);
-    const uint32_t sbyte = nan_blk ? 0xffu : (zero_blk ? 0u : (uint32_t)(sexp + 127));
-    // one lane per quad writes the scale byte; the others aim past the row (dropped)
-    st1_mx(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off >> 6) : kDropOffset);
+    for (int n = 0; n < N; ++n) {
+        u16x2 m = u16x2{0, 0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, ob[n][w] & 0x7fff7fffu));
+        amax[n] = max((uint32_t)m[0], (uint32_t)m[1]) << 16;
+    }
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0xB1>(amax[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) amax[n] = max(amax[n], dpp_u<0x4E>(amax[n]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const bool nan_blk = amax[n] > 0x7f800000u;
+        const bool zero_blk = amax[n] == 0u;
+        int sexp = __builtin_amdgcn_frexp_expf(__uint_as_float(amax[n])) - 1 - 2;  // floor(log2 amax) - 2
+        sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
+        const float sc = __uint_as_float((uint32_t)(sexp + 127) << 23);
+        uint32_t word = 0u;
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf_lo(ob[n][0]), bf_hi(ob[n][0]), sc, 0);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf_lo(ob[n][1]), bf_hi(ob[n][1]), sc, 1);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf_lo(ob[n][2]), bf_hi(ob[n][2]), sc, 2);
+        word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, bf_lo(ob[n][3]), bf_hi(ob[n][3]), sc, 3);
+        const uint32_t keep = (nan_blk || zero_blk) ? 0u : 0xffffffffu;
+        st4_mx(word & keep, r_q, off[n] >> 2);
+        const uint32_t sbyte = nan_blk ? 0xffu : (zero_blk ? 0u : (uint32_t)(sexp + 127));
+        // one lane per quad writes the scale byte; the others aim past the row (dropped)
+        st1_mx(sbyte, r_sc, ((int)threadIdx.x & 3) == 0 ? (off[n] >> 6) : kDropOffset);
+    }
 }
 
 // Normalised values of one vector slot, (y * rstd) * gamma each rounded once to bf16, packed.
@@ -494,25 +504,13 @@ __device__ __forceinline__ u32x4 norm_slot(u32x4 yb, u32x4 gam, double rstd, flo
     return packed;
 }
 
-// Normalise one vector slot and store it as out; returns the packed bf16 values (the FP8
-// quant's input).
+// Normalise one vector slot and store it as out; returns the packed bf16 values (the FP8 and
+// MXFP4 quants' input).
 __device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, float r32, bool r32_ok,
                                             rsrc_t r_out, uint32_t off) {
     const u32x4 packed = norm_slot(yb, gam, rstd, r32, r32_ok);
     st16(packed, r_out, off);
     return packed;
-}
-
-// norm_store that also returns the values as floats in `o` (the MXFP4 quant's input).
-__device__ __forceinline__ void norm_store_f(u32x4 yb, u32x4 gam, double rstd, float r32, bool r32_ok,
-                                             rsrc_t r_out, uint32_t off, float (&o)[8]) {
-    const u32x4 packed = norm_slot(yb, gam, rstd, r32, r32_ok);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        o[2 * w] = bf_lo(packed[w]);
-        o[2 * w + 1] = bf_hi(packed[w]);
-    }
-    st16(packed, r_out, off);
 }
 
 // Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
@@ -582,18 +580,22 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
 #pragma unroll
         for (int v = 0; v < VPL; ++v) offs[v] = off0 + v * L16;
         quant_slots<kCodeP, VPL>(ob, r_q, r_sc, offs, sbase, sstride);
+    } else if constexpr (QM == kQuantMxfp4) {
+        u32x4 ob[VPL];
+        uint32_t offs[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
+            ob[v] = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
+            offs[v] = off0 + v * L16;
+        }
+        mxfp4_slots<VPL>(ob, r_q, r_sc, offs);
     } else {
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
-            if constexpr (QM == kQuantMxfp4) {
-                float o[8];
-                norm_store_f(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16, o);
-                mxfp4_slot(o, r_q, r_sc, off0 + v * L16);
-            } else {
-                const u32x4 ob = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
-                if constexpr (QM == kQuantFp8) quant_slot<kCodeP>(ob, r_q, r_sc, off0 + v * L16, sbase, sstride);
-            }
+            const u32x4 ob = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
+            if constexpr (QM == kQuantFp8) quant_slot<kCodeP>(ob, r_q, r_sc, off0 + v * L16, sbase, sstride);
         }
     }
 }
