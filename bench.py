@@ -39,7 +39,7 @@ from gen import CONFIGS, SWEEP_T, Config, make_inputs, sweep_config  # noqa: E40
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, AMD's published figure
 METRIC = "effective HBM GB/s (% of MI355X peak) and µs/call of fused reduce+RMSNorm"
-KERNEL_SRC = os.path.join(ROOT, "tp_all_reduce_amd", "csrc", "farn_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "tp_all_reduce_amd", "csrc", f) for f in ("farn_kernels.hip", "farn_device_math.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = {
@@ -64,11 +64,11 @@ def log(msg):
 
 
 def kernel_hash() -> str:
-    """sha256[:16] of the kernel source's code: comments, blank lines and trailing blanks
-    removed, so that recorded counters stay tied to the code they were taken on and not to
-    its comments."""
+    """sha256[:16] of the kernels' source code (the kernel file and its device-math header):
+    comments, blank lines and trailing blanks removed, so that recorded counters stay tied to
+    the code they were taken on and not to its comments."""
     import re
-    text = open(KERNEL_SRC).read()
+    text = "".join(open(p).read() for p in KERNEL_SRCS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../tp_all_reduce_amd/csrc/farn_device_math.h"
+
 // out[i] = E4M3 code of the fp32 with bit pattern base + i, i < n (n even)
 __global__ void fp8_of_bits(uint32_t base, uint8_t *out, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -32,37 +34,27 @@ __global__ void fp4_all_scales(const float *x, uint8_t *out, uint32_t n) {
 }
 
 // out[2i] = the hardware reciprocal square root (v_rsq_f64) of m[i], out[2i+1] = 1/sqrt(m[i]) as
-// the fused kernels form it for 2^-1000 <= m <= 2^1000: v_rsq_f64 refined by two Newton steps
+// the fused kernels form it for 2^-1000 <= m <= 2^1000 (farn_math::rsq_newton, the kernels' own
+// function)
 __global__ void rsq_newton(const double *m, double *out, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const double x = m[i];
-    const double hm = 0.5 * x;
-    const double y0 = __builtin_amdgcn_rsq(x);
-    const double y1 = __builtin_fma(y0, __builtin_fma(-hm * y0, y0, 0.5), y0);
-    out[2 * i] = y0;
-    out[2 * i + 1] = __builtin_fma(y1, __builtin_fma(-hm * y1, y1, 0.5), y1);
+    out[2 * i] = __builtin_amdgcn_rsq(m[i]);
+    out[2 * i + 1] = farn_math::rsq_newton(m[i]);
 }
 
 // For amax = the fp32 whose bits are amax_bits[i] (a bf16 magnitude pattern shifted left 16):
 // out[3i] = scale = amax/448 and out[3i+1] = 1/(scale * k) as the FP8 quant forms them, with k =
-// 2^64 for scale < 2^-64 (else 1); out[3i+2] = scale * k. The same sequence as quant_slots in
-// the library's kernel source.
+// 2^64 for scale < 2^-64 (else 1) and 0 for a zero scale; out[3i+2] = scale * k. The kernels'
+// own functions (farn_math::fp8_scale, farn_math::fp8_recip) and the quant's rescaling rule.
 __global__ void fp8_scale_inv(const uint32_t *amax_bits, float *out, uint32_t n) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const uint32_t amax = amax_bits[i];
-    const float c = 0x1.24924ap-9f;
-    const float a = __uint_as_float(amax);
-    const float q0 = a * c;
-    const float r = __builtin_fmaf(-q0, 448.0f, a);
-    const float scale = amax < 0x7f800000u ? __builtin_fmaf(r, c, q0) : q0;
+    const float scale = farn_math::fp8_scale(amax_bits[i]);
     const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
     const float sk = scale * k;
-    const float y = __builtin_amdgcn_rcpf(sk);
-    const float yn = __builtin_fmaf(__builtin_fmaf(-sk, y, 1.0f), y, y);
     out[3 * i] = scale;
-    out[3 * i + 1] = scale == 0.0f ? 0.0f : (__builtin_isfinite(sk) ? yn : y);
+    out[3 * i + 1] = scale == 0.0f ? 0.0f : farn_math::fp8_recip(sk);
     out[3 * i + 2] = sk;
 }
 

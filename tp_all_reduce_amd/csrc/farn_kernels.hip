@@ -45,6 +45,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "farn_device_math.h"
 #include "farn_internal.h"
 
 namespace {
@@ -319,23 +320,13 @@ __device__ __forceinline__ double row_rstd(double ss, const Params &k, double *s
     const double m = __builtin_fma(tot, k.inv_h, (double)k.eps);
     double r;
     if (m >= 0x1p-1000 && m <= 0x1p1000) {  // the same in every lane of the row
-        const double hm = 0.5 * m;
-        const double y0 = __builtin_amdgcn_rsq(m);
-        const double y1 = __builtin_fma(y0, __builtin_fma(-hm * y0, y0, 0.5), y0);
-        r = __builtin_fma(y1, __builtin_fma(-hm * y1, y1, 0.5), y1);
+        r = farn_math::rsq_newton(m);
     } else {
         __asm__ volatile("" ::: "memory");  // keeps this rare path a branch, not computed beside the other
         r = 1.0 / __builtin_sqrt(tot / k.h + (double)k.eps);
     }
     return r;
 }
-
-// RN(1/448): the scale amax/448 is formed as q0 = amax * c corrected by one FMA of the
-// remainder, q0 + (amax - q0 * 448) * c. Over every finite bf16 amax (32,640 values, zero and
-// subnormals included) this equals the correctly rounded quotient (checked in exact rational
-// arithmetic, tests/test_encoder_models.py, and on the GPU for every 16-bit magnitude
-// pattern, tests/test_gpu_conversions.py); inf and NaN take q0 (inf, or the quieted NaN).
-constexpr float kInv448 = 0x1.24924ap-9f;
 
 // E4M3 codes of N vector slots (8 bf16 values each, two per word of `ob`) and, from one lane
 // per 16-lane group, each group's scale, stored at byte sbase + group * sstride of r_sc. The
@@ -379,15 +370,10 @@ __device__ __forceinline__ void quant_slots(const u32x4 (&ob)[N], rsrc_t r_q, rs
     float scale[N], k[N], inv[N], sr[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        const float a = __uint_as_float(amax[n]);
-        const float q0 = a * kInv448;
-        const float r = __builtin_fmaf(-q0, 448.0f, a);
-        scale[n] = amax[n] < 0x7f800000u ? __builtin_fmaf(r, kInv448, q0) : q0;
+        scale[n] = farn_math::fp8_scale(amax[n]);  // amax/448, correctly rounded
         k[n] = scale[n] < 0x1p-64f ? 0x1p64f : 1.0f;
         const float sk = scale[n] * k[n];
-        const float y = __builtin_amdgcn_rcpf(sk);
-        const float yn = __builtin_fmaf(__builtin_fmaf(-sk, y, 1.0f), y, y);
-        inv[n] = scale[n] == 0.0f ? 0.0f : (__builtin_isfinite(sk) ? yn : y);
+        inv[n] = scale[n] == 0.0f ? 0.0f : farn_math::fp8_recip(sk);
         sr[n] = min(sk, 0x1.fffffep127f);
     }
 #pragma unroll
