@@ -255,10 +255,28 @@ __device__ __forceinline__ void load_slot(SlotIn<R> &in, const Params &k, int64_
     in.res = ld16(row_rsrc(k.res, k.res ? ro : 0, k.res ? rb : 0), off);
 }
 
-// fp32 sum of the partials in rank order, residual last (skipped, not a +0, when there
-// is none), rounded to bf16: four packed pairs. Lanes past the row end see zeros.
-template <int R>
+// Forms of the fold (the same sums; they differ in instructions and so in how the compiler
+// schedules the row's loads around them):
+//   kFoldSelect  - the residual term added, then the sum with or without it selected
+//   kFoldNegZero - with no residual the zero words loaded in its place are unpacked as -0 (the
+//                  sign bit or-ed in; x + (-0) is x for every x, -0 and NaN included), no select
+//   kFoldNegZeroReg - the same with the high-half mask in a register, so that mask-and-or is one
+//                  instruction (a three-operand instruction cannot take the 32-bit constant
+//                  itself on this target)
+//   kFoldNoResidual - no residual term (the standalone all-reduce)
+// Chosen per kernel by measurement on MI355X (do_row).
+constexpr int kFoldSelect = 0;
+constexpr int kFoldNegZero = 1;
+constexpr int kFoldNegZeroReg = 2;
+constexpr int kFoldNoResidual = 3;
+
+// fp32 sum of the partials in rank order, residual last (a missing residual adds nothing, so a
+// -0 sum stays -0), rounded to bf16: four packed pairs. Lanes past the row end see zeros.
+template <int R, int kFold>
 __device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
+    const uint32_t zsign = has_res ? 0u : 0x80000000u;
+    uint32_t hmask = 0xffff0000u;
+    if constexpr (kFold == kFoldNegZeroReg) __asm__("v_mov_b32 %0, 0xffff0000" : "=v"(hmask));
     u32x4 packed;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -269,19 +287,26 @@ __device__ __forceinline__ u32x4 fold_slot(const SlotIn<R> &in, bool has_res) {
             lo = lo + bf_lo(in.p[r][w]);
             hi = hi + bf_hi(in.p[r][w]);
         }
-        const float lo_r = lo + bf_lo(in.res[w]);
-        const float hi_r = hi + bf_hi(in.res[w]);
-        packed[w] = pack_bf16(has_res ? lo_r : lo, has_res ? hi_r : hi);
+        if constexpr (kFold == kFoldSelect) {
+            const float lo_r = lo + bf_lo(in.res[w]);
+            const float hi_r = hi + bf_hi(in.res[w]);
+            lo = has_res ? lo_r : lo;
+            hi = has_res ? hi_r : hi;
+        } else if constexpr (kFold != kFoldNoResidual) {
+            lo = lo + __uint_as_float((in.res[w] << 16) | zsign);
+            hi = hi + __uint_as_float((in.res[w] & hmask) | zsign);
+        }
+        packed[w] = pack_bf16(lo, hi);
     }
     return packed;
 }
 
 // fold_slot, stored as residual_out here (kStoreNow) or by the caller later, with the squares
 // of the rounded values added to ss (fp64; zeros from lanes past the row end add nothing).
-template <int R, bool kStoreNow>
+template <int R, bool kStoreNow, int kFold>
 __device__ __forceinline__ u32x4 reduce_slot(const SlotIn<R> &in, const Params &k, rsrc_t ro_out,
                                              uint32_t off, double &ss) {
-    const u32x4 packed = fold_slot<R>(in, k.res != nullptr);
+    const u32x4 packed = fold_slot<R, kFold>(in, k.res != nullptr);
     if constexpr (kStoreNow) st16(packed, ro_out, off);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -524,20 +549,28 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     constexpr bool kDefer = VPL == 2 && (QM == kQuantNone || kSmall);
     constexpr bool kOutsFirst = kSmall && QM == kQuantFp8 && VPL == 2;
     constexpr int kCodeP = kSmall ? kStoreCodeSmallPolicy : kStoreCodePolicy;
+    // Fold form (measured, interleaved, median of 5, against the select in every kernel): the -0
+    // unpack takes 1-3 % off FP8 and MXFP4 calls at decode sizes (up to 6 % at R = 4, T = 16,
+    // H = 4096 from HBM) and 1-7 % off few-rank plain calls there; with the mask in a register in
+    // the plain kernels, R = 8 calls of the two-slot kernel ran 1-4 % slower (other register
+    // allocation); the two-slot streaming quant kernels keep the select (with the -0 unpack
+    // 0.6 % slower on the FP8 and MXFP4 prefill chunk).
+    constexpr int kFold = QM == kQuantNone ? kFoldNegZero
+                                           : (VPL == 2 && !kSmall ? kFoldSelect : kFoldNegZeroReg);
     double ss = 0.0;
     u32x4 yb[VPL];
     if constexpr (VPL == 2) {
         SlotIn<R> in1;
         load_slot<R>(in1, k, t, off0 + L16);
-        yb[0] = reduce_slot<R, !kDefer>(in0, k, r_ro, off0, ss);
-        yb[1] = reduce_slot<R, !kDefer>(in1, k, r_ro, off0 + L16, ss);
+        yb[0] = reduce_slot<R, !kDefer, kFold>(in0, k, r_ro, off0, ss);
+        yb[1] = reduce_slot<R, !kDefer, kFold>(in1, k, r_ro, off0 + L16, ss);
     } else {
-        yb[0] = reduce_slot<R, true>(in0, k, r_ro, off0, ss);
+        yb[0] = reduce_slot<R, true, kFold>(in0, k, r_ro, off0, ss);
 #pragma unroll
         for (int v = 1; v < VPL; ++v) {
             SlotIn<R> in;
             load_slot<R>(in, k, t, off0 + v * L16);
-            yb[v] = reduce_slot<R, true>(in, k, r_ro, off0 + v * L16, ss);
+            yb[v] = reduce_slot<R, true, kFold>(in, k, r_ro, off0 + v * L16, ss);
         }
     }
     const double rstd = row_rstd(ss, k, slot);
@@ -620,7 +653,7 @@ __global__ __launch_bounds__(1024) void farn_reduce_rows(const Params k) {
         const uint32_t off = (v * blockDim.x + threadIdx.x) * 16u;
         SlotIn<R> in;
         load_slot<R>(in, k, t, off);
-        st16(fold_slot<R>(in, false), r_out, off);
+        st16(fold_slot<R, kFoldNoResidual>(in, false), r_out, off);
     }
 }
 
