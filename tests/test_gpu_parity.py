@@ -411,6 +411,41 @@ def test_signed_zeros_bit_exact(dev):
 
 
 # ------------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("R,T,H", [(1, 5, 1024), (3, 5, 1024), (3, 520, 1024), (2, 3, 20480)])
+def test_signed_zeros_no_residual(dev, R, T, H):
+    """With no residual, elements whose partials are all -0 sum to -0 (nothing is added to them:
+    a +0 would turn the sum into +0), so residual_out, out and the codes are the -0 ones, bit for
+    bit as the oracle gives. The shapes reach every form of the kernels' fold: both launch
+    shapes, the FP8 / MXFP4 small-call schedule (T <= 512) and streaming schedule (T = 520),
+    four vectors per lane (H = 20480), and the standalone all-reduce."""
+    d = make_inputs(CONFIGS["tiny"], seed=62, R=R, T=T, H=H)
+    P = d["partials"]
+    for t in range(T):
+        P[:, t, np.arange(t % 7, H, 5 + t % 7)] = 0x8000
+    u = Uploaded(d, dev, residual=False)
+    rows = np.arange(T)
+    ref_q = u.oracle_rows(rows, True)
+    ref_p = u.oracle_rows(rows, False)
+    ref_mx = oracle.reduce_add_rmsnorm_mxfp4(P, None, d["gamma"], EPS, nthreads=ORACLE_THREADS)
+    assert (ref_p[0] == 0x8000).sum() >= T * H // 12 and (ref_p[1] == 0x8000).sum() >= T * H // 12
+    assert (ref_q[2] == 0x80).sum() >= T * H // 12
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
+        say(f"[gpu] signed zeros without residual, R={R} T={T} H={H} variant={variant}")
+        ro, out = F.reduce_add_rmsnorm(u.P, None, u.g, EPS, variant=variant)
+        qro, qout, q, sc = F.reduce_add_rmsnorm_quant_group(u.P, None, u.g, EPS, variant=variant)
+        mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(u.P, None, u.g, EPS, variant=variant)
+        torch.cuda.synchronize()
+        for name, got, want in (("residual_out", ro, ref_p[0]), ("out", out, ref_p[1]),
+                                ("FP8 residual_out", qro, ref_q[0]), ("FP8 out", qout, ref_q[1]),
+                                ("MXFP4 residual_out", mro, ref_mx[0]), ("MXFP4 out", mout, ref_mx[1])):
+            assert np.array_equal(from_dev_bf16(got), want), f"{name} differs, variant {variant}"
+        assert np.array_equal(q.cpu().numpy(), ref_q[2]) and np.array_equal(sc.cpu().numpy(), ref_q[3])
+        assert np.array_equal(mq.cpu().numpy(), ref_mx[2]) and np.array_equal(msc.cpu().numpy(), ref_mx[3])
+    red = F.reduce(u.P)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bf16(red), oracle.reduce(P)), "all-reduce differs"
+
+
 def test_graph_capture_replays_match_eager(dev):
     """The calls allocate nothing and never synchronise, so a serving loop can capture them in a
     HIP graph. Replay several times with the program's own eager work and synchronisations
