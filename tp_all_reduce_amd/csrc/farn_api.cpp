@@ -135,9 +135,9 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //   Everything else: wide (the narrow shape median 3.9 % slower, up to 36 % at small T and
 //   H <= 2048).
 // Against the faster shape at each point the rule loses 0.48 % on average over the 820 points,
-// 0.50 .. 0.58 % over the 320 random ones, and 0.28 .. 0.46 % (at most 13 .. 16.5 %: R = 3,
-// H = 4608, T = 434, plain) over 160 further random points measured after it was fixed, on two
-// boxes. The previous rule, without
+// 0.50 .. 0.58 % over the 320 random ones, and 0.28 .. 0.49 % (at most 10.6 .. 16.5 %, mostly at
+// R = 3, H = 4608, T = 434, plain) over 160 further random points measured after it was fixed,
+// in four timings on three boxes. The previous rule, without
 // band 3 and with a band for H = 1544 .. 2048 from T = 4096 (-1 .. -5 %), lost 1.19 %,
 // 0.95 .. 1.18 % and 1.05 % (at most 19 % on the last set).
 int select(int R, int64_t T, int64_t H, int quant) {
