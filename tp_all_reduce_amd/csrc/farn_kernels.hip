@@ -554,8 +554,9 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     // H = 4096 from HBM) and 1-7 % off few-rank plain calls there; with the mask in a register in
     // the plain kernels, R = 8 calls of the two-slot kernel ran 1-4 % slower (other register
     // allocation); the two-slot streaming quant kernels keep the select (with the -0 unpack
-    // 0.6 % slower on the FP8 and MXFP4 prefill chunk).
-    constexpr int kFold = QM == kQuantNone ? kFoldNegZero
+    // 0.6 % slower on the FP8 and MXFP4 prefill chunk), and so does the plain kernel of a single
+    // rank (0.4-3 % slower with it at H = 7168, T = 2048 and 8192).
+    constexpr int kFold = QM == kQuantNone ? (R == 1 ? kFoldSelect : kFoldNegZero)
                                            : (VPL == 2 && !kSmall ? kFoldSelect : kFoldNegZeroReg);
     double ss = 0.0;
     u32x4 yb[VPL];
