@@ -23,7 +23,7 @@
  *   y     = acc + residual[t,h]                          fp32 (no add if residual == NULL)
  *   residual_out[t,h] = bf16_rne(y)
  *   rstd  = 1 / sqrt(sum_h residual_out[t,h]^2 / H + eps)   fp64: sum in a fixed reduction
- *           tree, the mean and reciprocal square root within about one fp64 unit
+ *           tree, the mean by one fp64 FMA, the reciprocal square root within two fp64 units
  *   out[t,h] = bf16_rne((residual_out[t,h] * rstd) * gamma[h])   one rounding of the product
  *           (formed in fp32 where that provably gives the same bf16 value, else in fp64)
  * and for the quant call, per group g of 128 channels:
