@@ -6,6 +6,7 @@ never dereference them, and every call below is rejected before any HIP call."""
 from __future__ import annotations
 
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -305,6 +306,57 @@ def test_bench_refuses_several_gpus():
     proc = subprocess.run([os.sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                           capture_output=True, text=True, timeout=300)
     assert proc.returncode == 2 and "one GPU" in proc.stderr
+
+
+def _bench_module():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(root, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_kernel_hash_ignores_comments_only(tmp_path, monkeypatch):
+    """The hash that ties recorded HBM counters to the kernels changes with the code and not
+    with its comments, blank lines or trailing blanks."""
+    B = _bench_module()
+    copies = []
+    for src in B.KERNEL_SRCS:
+        dst = tmp_path / os.path.basename(src)
+        dst.write_text(open(src).read())
+        copies.append(str(dst))
+    monkeypatch.setattr(B, "KERNEL_SRCS", copies)
+    base = B.kernel_hash()
+    assert base == _bench_module().kernel_hash()  # the copies hash as the sources do
+    text = open(copies[0]).read()
+    commented = text.replace("constexpr int kMaxWaves = 16;",
+                             "// a comment line\n\nconstexpr int kMaxWaves = 16;   /* and a block\n comment */  ")
+    assert commented != text
+    open(copies[0], "w").write(commented)
+    assert B.kernel_hash() == base
+    open(copies[0], "w").write(text.replace("constexpr int kMaxWaves = 16;", "constexpr int kMaxWaves = 32;"))
+    assert B.kernel_hash() != base
+    open(copies[0], "w").write(text)
+    header = open(copies[1]).read()
+    open(copies[1], "w").write(header.replace("0x1.24924ap-9f", "0x1.24924cp-9f"))
+    assert B.kernel_hash() != base  # the device-math header is part of the kernels' code
+
+
+def test_recorded_traffic_only_for_the_kernels_it_was_taken_on(tmp_path, monkeypatch):
+    """roofline.traffic comes from counters recorded under a kernel hash; for any other hash
+    (the kernels changed since) the bench reports none."""
+    B = _bench_module()
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(B, "TRAFFIC_FILE", str(path))
+    assert B.recorded_traffic("prefill_fp8") is None  # no file
+    path.write_text(json.dumps({"prefill_fp8": {"kernel_sha": B.kernel_hash(), "bytes_per_launch": 123}}))
+    assert B.recorded_traffic("prefill_fp8") == 123
+    assert B.recorded_traffic("prefill") is None  # no record for that workload
+    path.write_text(json.dumps({"prefill_fp8": {"kernel_sha": "0" * 16, "bytes_per_launch": 123}}))
+    assert B.recorded_traffic("prefill_fp8") is None
+    path.write_text("{not json")
+    assert B.recorded_traffic("prefill_fp8") is None
 
 
 def test_c_client_builds_against_header_alone(tmp_path):
