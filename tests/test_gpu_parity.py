@@ -20,8 +20,8 @@ import torch
 import oracle
 import tp_all_reduce_amd as F
 from gen import CONFIGS, SWEEP_T, make_inputs, sweep_config
-from parity import (compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16, mxfp4_within_tolerance,
-                    to_dev_bf16, within_tolerance)
+from parity import (bits_to_f32, compare_bf16, compare_fp8, compare_mxfp4, from_dev_bf16,
+                    mxfp4_within_tolerance, to_dev_bf16, within_tolerance)
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -444,6 +444,78 @@ def test_signed_zeros_no_residual(dev, R, T, H):
     red = F.reduce(u.P)
     torch.cuda.synchronize()
     assert np.array_equal(from_dev_bf16(red), oracle.reduce(P)), "all-reduce differs"
+
+
+def _bf16_of(x):
+    return (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _extreme_inputs():
+    """Rows of ordinary, huge (2^60), tiny (2^-100), zero and subnormal (2^-131) magnitude, and a
+    gamma holding zeros of both signs, negatives, subnormals, the largest finite values, infinities,
+    a NaN, and blocks of tiny (2^-100) and huge (2^100) values."""
+    R, T, H = 2, 6, 1024
+    rng = np.random.default_rng(71)
+    scale = np.array([1.0, 2.0 ** 60, 2.0 ** -100, 1.0, 0.0, 2.0 ** -131], np.float32)
+    P = _bf16_of(rng.standard_normal((R, T, H)).astype(np.float32) * scale[None, :, None])
+    g = _bf16_of(rng.uniform(0.5, 1.5, H).astype(np.float32))
+    for i, v in enumerate([0x0000, 0x8000, 0xBF80, 0x0001, 0x0080, 0x7F7F, 0xFF7F, 0x7F80, 0xFF80, 0x7FC0,
+                           0x0010, 0x1F80, 0x6F80]):
+        g[i * 7] = v
+    g[700:760] = _bf16_of(np.float32(2.0 ** -100) * rng.uniform(1, 2, 60).astype(np.float32))
+    g[800:860] = _bf16_of(np.float32(2.0 ** 100) * rng.uniform(1, 2, 60).astype(np.float32))
+    return P, g
+
+
+def _same_codes(gq, rq, gs, rs, nan_code):
+    """Codes and scales equal bit for bit, NaN codes and NaN scales compared as NaN."""
+    gq, rq = np.asarray(gq), np.asarray(rq)
+    nr, ng = nan_code(rq), nan_code(gq)
+    assert np.array_equal(nr, ng) and np.array_equal(gq[~nr], rq[~nr]), "codes differ"
+    gs, rs = np.asarray(gs), np.asarray(rs)
+    if gs.dtype == np.float32:
+        assert np.array_equal(np.isnan(gs), np.isnan(rs))
+        assert np.array_equal(gs[~np.isnan(rs)].view(np.uint32), rs[~np.isnan(rs)].view(np.uint32)), "scales differ"
+    else:
+        assert np.array_equal(gs, rs), "scale bytes differ"
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.0])
+def test_gamma_and_rstd_extremes(dev, eps):
+    """Where the normalisation's fp32 fast path cannot be trusted it must hand over to fp64: y*gamma
+    overflowing fp32 while the output is finite (rows of 2^60 with huge gamma), y*gamma subnormal
+    or underflowing to zero while the output is not (tiny rows and gamma), an fp32 rstd that is
+    infinite or above the fp32 range (eps = 0 with a zero or subnormal row), zero, negative,
+    infinite and NaN gamma. Every output equals the oracle bit for bit (NaN as NaN), plain, FP8
+    and MXFP4, in both launch shapes."""
+    P, g = _extreme_inputs()
+    R, T, H = P.shape
+    ref_p = oracle.reduce_add_rmsnorm(P, None, g, eps, nthreads=ORACLE_THREADS)
+    ref_q = oracle.reduce_add_rmsnorm_quant_group(P, None, g, eps, 128, True, nthreads=ORACLE_THREADS)
+    ref_m = oracle.reduce_add_rmsnorm_mxfp4(P, None, g, eps, nthreads=ORACLE_THREADS)
+    # the hazards are present: overflowing and underflowing fp32 products with finite, nonzero outputs
+    y, gf = bits_to_f32(ref_p[0]), bits_to_f32(g)
+    outf = bits_to_f32(ref_p[1])
+    with np.errstate(all="ignore"):
+        yg = y * gf[None, :]
+    over = np.isinf(yg) & np.isfinite(y) & np.isfinite(gf)[None, :]
+    under = (np.abs(yg) < 2.0 ** -126) & (y != 0) & (gf != 0)[None, :]
+    assert np.isfinite(outf[over]).sum() >= 32 and (outf[under] != 0).sum() >= 500
+    Pd = [to_dev_bf16(P[r], dev) for r in range(R)]
+    gd = to_dev_bf16(g, dev)
+    fp8_nan = lambda c: (c & 0x7F) == 0x7F
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
+        say(f"[gpu] gamma and rstd extremes, eps={eps} variant={variant}")
+        ro, out = F.reduce_add_rmsnorm(Pd, None, gd, eps, variant=variant)
+        qro, qout, q, sc = F.reduce_add_rmsnorm_quant_group(Pd, None, gd, eps, variant=variant)
+        mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(Pd, None, gd, eps, variant=variant)
+        torch.cuda.synchronize()
+        for name, got, want in (("residual_out", ro, ref_p[0]), ("out", out, ref_p[1]),
+                                ("FP8 out", qout, ref_q[1]), ("MXFP4 out", mout, ref_m[1])):
+            rep = compare_bf16(name, from_dev_bf16(got), want)
+            assert rep["n_bit_diff"] == 0, rep
+        _same_codes(q.cpu().numpy(), ref_q[2], sc.cpu().numpy(), ref_q[3], fp8_nan)
+        _same_codes(mq.cpu().numpy(), ref_m[2], msc.cpu().numpy(), ref_m[3], lambda c: np.zeros(c.shape, bool))
 
 
 def test_graph_capture_replays_match_eager(dev):
