@@ -654,6 +654,40 @@ def test_quant_every_group_max(dev):
     assert ((gq[ref_nan] & 0x7F) == 0x7F).all()
 
 
+def test_mxfp4_every_block_max(dev):
+    """One 32-channel MXFP4 block for each of the 32,768 bf16 magnitude patterns as its maximum
+    (zero, subnormals, normals, inf, every NaN), its other channels random below it with random
+    signs. With every partial 1.0, no residual and eps = 0 a row's mean square is exactly 1, so
+    rstd = 1 and the normalised output is gamma itself: gamma sets the blocks, 1,024 per call of
+    H = 32768. Codes and scale bytes equal the oracle's bit for bit, and so do the FP8 codes and
+    scales of the same outputs (groups of four such blocks)."""
+    rng = np.random.default_rng(92)
+    H = 32768
+    nb = H // 32
+    P1 = np.full((1, 1, H), 0x3F80, np.uint16)
+    Pd = [to_dev_bf16(P1[0], dev)]
+    say(f"[gpu] MXFP4 every block maximum, {0x8000 // nb} calls of H={H}")
+    for c in range(0x8000 // nb):
+        p = np.arange(c * nb, (c + 1) * nb, dtype=np.uint32)
+        mag = rng.integers(0, 1 << 16, size=(nb, 32), dtype=np.uint32) % (p[:, None] + 1)
+        mag[np.arange(nb), rng.integers(0, 32, size=nb)] = p
+        sign = rng.integers(0, 2, size=mag.shape, dtype=np.uint32) << 15
+        g = (mag | sign).astype(np.uint16).reshape(H)
+        gd = to_dev_bf16(g, dev)
+        _, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(Pd, None, gd, 0.0)
+        _, qout, q, sc = F.reduce_add_rmsnorm_quant_group(Pd, None, gd, 0.0)
+        torch.cuda.synchronize()
+        ref_m = oracle.reduce_add_rmsnorm_mxfp4(P1, None, g, 0.0, nthreads=ORACLE_THREADS)
+        ref_q = oracle.reduce_add_rmsnorm_quant_group(P1, None, g, 0.0, 128, True, nthreads=ORACLE_THREADS)
+        gnan = (g & 0x7FFF) > 0x7F80
+        assert np.array_equal(ref_m[1][0][~gnan], g[~gnan])  # out is gamma
+        for name, got in (("MXFP4 out", mout), ("FP8 out", qout)):
+            rep = compare_bf16(name, from_dev_bf16(got), ref_m[1])
+            assert rep["n_bit_diff"] == 0, (c, rep)
+        _same_codes(mq.cpu().numpy(), ref_m[2], msc.cpu().numpy(), ref_m[3], lambda x: np.zeros(x.shape, bool))
+        _same_codes(q.cpu().numpy(), ref_q[2], sc.cpu().numpy(), ref_q[3], lambda x: (x & 0x7F) == 0x7F)
+
+
 # ------------------------------------------------------------------ MXFP4 output
 def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label="", ref=None):
     say(f"[gpu] mxfp4 {label} R={u.R} T={u.T} H={u.H} variant={variant} emit={emit_out}")
