@@ -555,7 +555,8 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
     // the plain kernels, R = 8 calls of the two-slot kernel ran 1-4 % slower (other register
     // allocation); the two-slot streaming quant kernels keep the select (with the -0 unpack
     // 0.6 % slower on the FP8 and MXFP4 prefill chunk), and so does the plain kernel of a single
-    // rank (0.4-3 % slower with it at H = 7168, T = 2048 and 8192).
+    // rank (0.4-3 % slower with it at H = 7168, T = 2048 and 8192). The four-slot kernels (rows
+    // beyond 16384 channels, not measured) take the forms of the one-slot ones.
     constexpr int kFold = QM == kQuantNone ? (R == 1 ? kFoldSelect : kFoldNegZero)
                                            : (VPL == 2 && !kSmall ? kFoldSelect : kFoldNegZeroReg);
     double ss = 0.0;
