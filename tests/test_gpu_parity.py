@@ -781,6 +781,38 @@ def test_random_shapes(dev):
             run_mxfp4(u, variant, emit_out=bool(i % 2), label=f"rand{i}")
 
 
+def test_random_shapes_many_rows_bit_exact(dev):
+    """Seeded random calls of many rows (T log-uniform over 300 .. 4000, H a multiple of 128 up
+    to 32768, R = 1 .. 8, with and without residual; the automatic shape and both forced ones):
+    the streaming two-slot kernels, the reserved-LDS launches and the four-slot kernels, every
+    output bit for bit equal to the oracle's (plain, FP8 with and without the bf16 output,
+    MXFP4)."""
+    rng = np.random.default_rng(2025)
+    for i in range(18):
+        R = int(rng.integers(1, 9))
+        T = int(np.exp(rng.uniform(np.log(300), np.log(4000))))
+        H = int(rng.integers(1, 65)) * 128 if i % 6 else int(rng.integers(129, 257)) * 128
+        T = min(T, (24 << 20) // H)  # at most 24 M elements per array
+        d = make_inputs(CONFIGS["decode_fp8"], seed=5000 + i, R=R, T=T, H=H)
+        u = Uploaded(d, dev, residual=bool(i % 4))
+        variant = ["auto", "wide", "narrow"][i % 3]
+        emit = bool(i % 2)
+        rows = np.arange(T)
+        rep_ro, rep_out, _ = run_and_compare(u, False, variant, label=f"many{i}")
+        assert rep_ro["n_bit_diff"] == 0 and rep_out["n_bit_diff"] == 0, (i, R, T, H)
+        _, rep_out, rep_fp8 = run_and_compare(u, True, variant, emit_out=emit, label=f"many{i}")
+        assert rep_fp8["n_code_diff"] == 0 and rep_fp8["max_scale_rel_err"] == 0.0, (i, R, T, H, rep_fp8)
+        assert rep_out is None or rep_out["n_bit_diff"] == 0, (i, R, T, H)
+        ro, out, q, sc = F.reduce_add_rmsnorm_mxfp4(u.P, u.res, u.g, EPS, emit_out=emit, variant=VARIANTS[variant])
+        torch.cuda.synchronize()
+        ref = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"] if u.res is not None else None,
+                                              d["gamma"], EPS, emit, nthreads=ORACLE_THREADS)
+        assert np.array_equal(from_dev_bf16(ro), ref[0]), (i, "MXFP4 residual_out")
+        assert out is None or np.array_equal(from_dev_bf16(out), ref[1]), (i, "MXFP4 out")
+        assert np.array_equal(q.cpu().numpy(), ref[2]) and np.array_equal(sc.cpu().numpy(), ref[3]), (i, "MXFP4 codes")
+        del u, d
+
+
 # one point inside every band of the automatic shape rule (and the reserved-LDS launches), and
 # points just outside them: (R, T, H)
 RULE_BAND_POINTS = [
