@@ -688,6 +688,38 @@ def test_mxfp4_every_block_max(dev):
         _same_codes(q.cpu().numpy(), ref_q[2], sc.cpu().numpy(), ref_q[3], lambda x: (x & 0x7F) == 0x7F)
 
 
+def test_fp8_every_group_max_fused_one_slot(dev):
+    """Each of the 32,768 bf16 magnitude patterns (zero, subnormals, normals, inf, every NaN) as
+    the maximum of one 128-channel group through the fused FP8 call in the one-slot kernel (wide
+    shape, H = 8192, 64 groups a call), so both the quotient path without the 2^64 rescaling and
+    the rescaled one run on every group maximum. As above, all partials 1.0, no residual and
+    eps = 0 make the output gamma. Codes and scales equal the oracle's bit for bit (NaN codes as
+    NaN codes)."""
+    rng = np.random.default_rng(93)
+    H = 8192
+    ng = H // 128
+    P1 = np.full((1, 1, H), 0x3F80, np.uint16)
+    Pd = [to_dev_bf16(P1[0], dev)]
+    say(f"[gpu] FP8 every group maximum through the one-slot fused kernel, {0x8000 // ng} calls of H={H}")
+    gs, qs = [], []
+    for c in range(0x8000 // ng):
+        p = np.arange(c * ng, (c + 1) * ng, dtype=np.uint32)
+        mag = rng.integers(0, 1 << 16, size=(ng, 128), dtype=np.uint32) % (p[:, None] + 1)
+        mag[np.arange(ng), rng.integers(0, 128, size=ng)] = p
+        sign = rng.integers(0, 2, size=mag.shape, dtype=np.uint32) << 15
+        g = (mag | sign).astype(np.uint16).reshape(H)
+        _, out, q, sc = F.reduce_add_rmsnorm_quant_group(Pd, None, to_dev_bf16(g, dev), 0.0,
+                                                         variant=F.VARIANT_WIDE)
+        gs.append(g)
+        qs.append((out, q, sc))
+    torch.cuda.synchronize()
+    for c, (g, (out, q, sc)) in enumerate(zip(gs, qs)):
+        ref = oracle.reduce_add_rmsnorm_quant_group(P1, None, g, 0.0, 128, True, nthreads=ORACLE_THREADS)
+        rep = compare_bf16("out", from_dev_bf16(out), ref[1])
+        assert rep["n_bit_diff"] == 0, (c, rep)
+        _same_codes(q.cpu().numpy(), ref[2], sc.cpu().numpy(), ref[3], lambda x: (x & 0x7F) == 0x7F)
+
+
 # ------------------------------------------------------------------ MXFP4 output
 def run_mxfp4(u: Uploaded, variant="auto", emit_out=True, rows=None, label="", ref=None):
     say(f"[gpu] mxfp4 {label} R={u.R} T={u.T} H={u.H} variant={variant} emit={emit_out}")
