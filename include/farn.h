@@ -143,7 +143,8 @@ farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, co
  * (farn_select_variant) picks by measurement on MI355X. It takes NARROW for
  *   - 6144 < H <= 8192, except the plain call with H > 7168 from T = 4096;
  *   - 4608 < H <= 5120 with 768 <= T < 2048;
- *   - the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512;
+ *   - the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 from T = 80 or
+ *     256 <= T < 512;
  *   - R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536);
  * and WIDE everywhere else. Both compute the same results (their fp64 sums of squares differ
  * only in the order of additions). */

@@ -72,11 +72,12 @@ HEADER_RULE_POINTS = [
     # 4608 < H <= 5120 with 768 <= T < 2048
     (8, 768, 5120, False, N), (8, 2047, 4616, True, N), (8, 767, 5120, False, W), (8, 2048, 5120, False, W),
     (8, 1024, 4608, False, W), (8, 1024, 5128, False, W), (6, 1000, 4736, "mxfp4", N), (8, 767, 5120, True, W),
-    # the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512
-    (8, 16, 2560, True, N), (8, 16, 2560, False, W), (8, 16, 2560, "mxfp4", W), (8, 767, 3712, True, N),
+    # the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 from T = 80 or 256 <= T < 512
+    (8, 80, 2560, True, N), (8, 79, 2560, True, W), (8, 16, 2560, True, W), (2, 1, 3712, True, W),
+    (8, 80, 2560, False, W), (8, 80, 2560, "mxfp4", W), (8, 767, 3712, True, N),
     (8, 768, 3712, True, W), (8, 100, 3720, True, W), (8, 256, 6144, True, N), (8, 511, 4096, True, N),
     (8, 512, 4096, True, W), (8, 255, 4096, True, W), (8, 300, 2048, True, W), (8, 300, 2056, True, N),
-    (1, 1, 2056, True, N), (6, 300, 4096, "fp8", N), (6, 300, 4096, "mxfp4", W),
+    (1, 80, 2056, True, N), (1, 1, 2056, True, W), (6, 300, 4096, "fp8", N), (6, 300, 4096, "mxfp4", W),
     # R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536)
     (4, 512, 2056, False, N), (4, 767, 6144, False, N), (4, 768, 4096, False, W), (4, 511, 3072, False, W),
     (2, 1535, 4096, False, N), (2, 1536, 3072, False, W), (1, 512, 4096, False, N), (5, 512, 3072, False, W),
@@ -98,7 +99,7 @@ def test_header_states_the_rule():
     text = open(HEADER).read()
     for phrase in ("6144 < H <= 8192, except the plain call with H > 7168 from T = 4096",
                    "4608 < H <= 5120 with 768 <= T < 2048",
-                   "the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 or 256 <= T < 512",
+                   "the FP8 call with 2048 < H <= 6144 and T < 768, when H <= 3712 from T = 80 or 256 <= T < 512",
                    "R <= 4 and 2048 < H <= 6144 with 512 <= T < 768 (R <= 2: T < 1536)",
                    "and WIDE everywhere else", "quant: 0 for the plain call, 1 for the FP8 call, 2 for the MXFP4 call"):
         assert phrase in " ".join(text.replace("*", " ").split()), phrase

@@ -123,11 +123,15 @@ farn_status check(const void *const *partials, int R, const void *residual, cons
 //   2. nvec in (576, 640] (H = 4616 .. 5120) at 768 <= T < 2048: narrow, -3 .. -14 % at
 //      T = 768 .. 1024 (two of 16 points +1.3 and +2.1 %), -2.8 .. +1.5 % at T = 1400 .. 2000.
 //   3. The FP8 call with nvec in (256, 768] (H = 2056 .. 6144) below T = 768, when
-//      nvec <= 464 (H <= 3712) or 256 <= T < 512: narrow, median -5.7 %, down to -21 %, in
-//      five of six points faster; the two-slot kernel overlaps each slot's group reductions and
-//      scale with the other slot's loads. From T = 768 the wide shape is up to 10 % faster at
-//      H = 2560. The MXFP4 call is not in this band: its narrow shape is 3-7 % slower below
-//      T = 100 there.
+//      nvec <= 464 (H <= 3712) from T = 80, or 256 <= T < 512: narrow, median -5.7 %, down to
+//      -21 %, in five of six points faster; the two-slot kernel overlaps each slot's group
+//      reductions and scale with the other slot's loads. From T = 768 the wide shape is up to
+//      10 % faster at H = 2560. Below T = 80 the one-slot kernel, which skips the rescale
+//      multiplies, is the faster one at H <= 3712 (on a grid of 180 points, R = 2..8,
+//      H = 2176 .. 3712, T = 8 .. 256, cache-hot: narrow +0.7 .. +4.8 % by median up to T = 48,
+//      even at T = 64, -1.6 % from T = 96; the bound takes the rule's loss there from 1.50 % to
+//      0.22 %, on 80 further random points streaming from HBM from 4.17 % to 1.63 %). The MXFP4
+//      call is not in this band: its narrow shape is 3-7 % slower below T = 100 there.
 //   4. R <= 4, nvec in (256, 768] at 512 <= T < 768 (two ranks: T < 1536): narrow, median
 //      -3.2 %, down to -20 % (FP8, T = 512), up to +10 % at H = 2560. With few ranks the wide
 //      shape keeps only R + 1 loads in flight per lane; the narrow one doubles that. At T = 768
@@ -145,7 +149,7 @@ int select(int R, int64_t T, int64_t H, int quant) {
     if (nvec > 768 && nvec <= 1024)
         return (quant == kNone && nvec > 896 && T >= 4096) ? FARN_VARIANT_WIDE : FARN_VARIANT_NARROW;
     if (nvec > 576 && nvec <= 640 && T >= 768 && T < 2048) return FARN_VARIANT_NARROW;
-    if (quant == kFp8 && nvec > 256 && nvec <= 768 && T < 768 && (nvec <= 464 || (T >= 256 && T < 512)))
+    if (quant == kFp8 && nvec > 256 && nvec <= 768 && T < 768 && ((nvec <= 464 && T >= 80) || (T >= 256 && T < 512)))
         return FARN_VARIANT_NARROW;
     if (R <= 4 && nvec > 256 && nvec <= 768 && T >= 512 && T < (R <= 2 ? 1536 : 768)) return FARN_VARIANT_NARROW;
     return FARN_VARIANT_WIDE;
