@@ -775,11 +775,14 @@ def test_mxfp4_no_residual_no_out_and_special_blocks(dev):
     assert np.all(scn[2] == 0xFF)  # the NaN makes the whole row's out NaN
 
 
-@pytest.mark.parametrize("name", ["decode_ds", "decode_fp8"])
-def test_fp8_scales_column_major(dev, name):
+@pytest.mark.parametrize("name,shape", [("decode_ds", None), ("decode_fp8", None),
+                                        ("decode_ds", (8, 1100, 7168)), ("decode_ds", (3, 40, 20480))])
+def test_fp8_scales_column_major(dev, name, shape):
     """Column-major scales ([H/128, T]) hold the same values as the row-major ones, transposed;
-    codes and bf16 outputs are unchanged."""
-    u = Uploaded(make_inputs(CONFIGS[name], seed=95), dev)
+    codes and bf16 outputs are unchanged. The decode shapes, a call of many rows (the streaming
+    two-slot kernel with LDS reserved) and four vector slots per lane (H = 20480)."""
+    extra = {} if shape is None else dict(R=shape[0], T=shape[1], H=shape[2])
+    u = Uploaded(make_inputs(CONFIGS[name], seed=95, **extra), dev)
     say(f"[gpu] column-major scales {name}")
     r_ro, r_out, r_q, r_s = u.oracle_rows(np.arange(u.T), True)
     for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
