@@ -216,8 +216,10 @@ def test_quant_without_bf16_out(dev):
         run_and_compare(u, True, variant, emit_out=False, label="no-out")
 
 
-def test_in_place_residual(dev):
-    d = make_inputs(CONFIGS["decode_ds"], seed=10, T=33)
+@pytest.mark.parametrize("T,H", [(33, 7168), (600, 7168), (9, 20480)])
+def test_in_place_residual(dev, T, H):
+    """residual_out written over the residual: decode and many rows, two and four vector slots."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=10, T=T, H=H)
     ref_ro, ref_out = oracle.reduce_add_rmsnorm(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
     for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
         say(f"[gpu] in-place residual variant={variant}")
@@ -231,10 +233,13 @@ def test_in_place_residual(dev):
         assert ok, why
 
 
-def test_in_place_residual_quant(dev):
+@pytest.mark.parametrize("T,H", [(21, 7168), (600, 7168), (9, 20480)])
+def test_in_place_residual_quant(dev, T, H):
     """In place with the FP8 and MXFP4 calls too (their kernels store residual_out at a
-    different point of the row than the plain two-slot kernel)."""
-    d = make_inputs(CONFIGS["decode_ds"], seed=11, T=21)
+    different point of the row than the plain two-slot kernel): the small-call schedule, the
+    streaming one (each slot's residual_out stored right after its fold, T = 600) and four
+    vector slots per lane."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=11, T=T, H=H)
     ref = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
     ref_mx = oracle.reduce_add_rmsnorm_mxfp4(d["partials"], d["residual"], d["gamma"], EPS, nthreads=8)
     for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
