@@ -51,6 +51,9 @@ WORKLOADS = {
     "tiny": (CONFIGS["tiny"], False, True),
     "prefill_mxfp4": (CONFIGS["prefill"], "mxfp4", True),
     "decode_ds_mxfp4": (CONFIGS["decode_ds"], "mxfp4", True),
+    # the FP8 call with the bf16 output off (emit_bf16 false): its own, smaller byte count
+    "decode_fp8_noout": (CONFIGS["decode_fp8"], True, False),
+    "prefill_fp8_noout": (CONFIGS["prefill"], True, False),
 }
 for _T in SWEEP_T:
     WORKLOADS[f"sweep_T{_T}"] = (sweep_config(_T), False, True)
@@ -338,9 +341,9 @@ def recorded_traffic(workload):
 def secondary(dev, steps):
     """Decode shapes in us/call: eager (one Python call per launch, host-bound), and graph
     replay, hot (one buffer set, cache-resident) and cold (sets rotated over >= 1 GiB, so
-    every call streams from HBM); plus the plain prefill call."""
+    every call streams from HBM); plus the plain, MXFP4 and bf16-output-free FP8 prefill calls."""
     out = {}
-    for name in ("decode_ds", "decode_fp8"):
+    for name in ("decode_ds", "decode_fp8", "decode_fp8_noout"):
         cfg, quant, emit = WORKLOADS[name]
         d = make_inputs(cfg)
         b = Bufs(d, dev, quant, emit)
@@ -358,7 +361,7 @@ def secondary(dev, steps):
                      "bytes_per_call": nb}
         del sets, b
         torch.cuda.empty_cache()
-    for name in ("prefill", "prefill_mxfp4"):
+    for name in ("prefill", "prefill_mxfp4", "prefill_fp8_noout"):
         cfg, quant, emit = WORKLOADS[name]
         b = Bufs(make_inputs(cfg), dev, quant, emit)
         nb = nbytes(cfg, quant, emit)
