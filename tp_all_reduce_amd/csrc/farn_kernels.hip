@@ -545,10 +545,18 @@ __device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, fl
     return packed;
 }
 
+// gamma of the vector slot at byte offset `off`. The four-slot kernels (rows beyond 16384
+// channels, 1024 lanes, so at most 128 VGPRs per lane) load it slot by slot when they
+// normalise instead of holding all four slots' gamma through the row: measured on MI355X, that
+// removes their register spills (28-44 bytes per lane) and makes them 3-10 % faster.
+__device__ __forceinline__ u32x4 gamma_slot(const Params &k, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(k.gamma, 0, k.nvec * 16), off, 0, kGammaLoadPolicy);
+}
+
 // Whole row t with the loads of slot 0 already issued into `in0`. With two slots per
 // lane the source issues the second slot's loads before reducing the first; with four
-// (rows beyond 16384 channels) the slots are loaded and reduced one after the other, to
-// bound register use.
+// (rows beyond 16384 channels) the slots are loaded and reduced one after the other, and each
+// slot's gamma is loaded when it is normalised, to bound register use.
 template <int R, int VPL, int QM, bool kSmall>
 __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[VPL],
                                        const Params &k, int64_t t, double *slot) {
@@ -628,7 +636,8 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
-            ob[v] = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
+            const u32x4 g = VPL == 4 ? gamma_slot(k, off0 + v * L16) : gam[v];
+            ob[v] = norm_store(yb[v], g, rstd, r32, r32_ok, r_out, off0 + v * L16);
             offs[v] = off0 + v * L16;
         }
         mxfp4_slots<VPL>(ob, r_q, r_sc, offs);
@@ -636,7 +645,8 @@ __device__ __forceinline__ void do_row(const SlotIn<R> &in0, const u32x4 (&gam)[
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             if constexpr (kDefer) st16(yb[v], r_ro, off0 + v * L16);
-            const u32x4 ob = norm_store(yb[v], gam[v], rstd, r32, r32_ok, r_out, off0 + v * L16);
+            const u32x4 g = VPL == 4 ? gamma_slot(k, off0 + v * L16) : gam[v];
+            const u32x4 ob = norm_store(yb[v], g, rstd, r32, r32_ok, r_out, off0 + v * L16);
             if constexpr (QM == kQuantFp8) quant_slot<kCodeP, VPL == 1>(ob, r_q, r_sc, off0 + v * L16, sbase, sstride);
         }
     }
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(1024) void farn_rows(const Params k) {
     SlotIn<R> in;
     load_slot<R>(in, k, t, threadIdx.x * 16u);
     u32x4 gam[VPL];
-    load_gamma<VPL>(gam, k);
+    if constexpr (VPL != 4) load_gamma<VPL>(gam, k);  // four slots: gamma_slot, slot by slot
     do_row<R, VPL, QM, kSmall>(in, gam, k, t, slot);
 }
 
