@@ -826,9 +826,11 @@ def test_random_shapes_many_rows_bit_exact(dev):
     to 32768, R = 1 .. 8, with and without residual; the automatic shape and both forced ones):
     the streaming two-slot kernels, the reserved-LDS launches and the four-slot kernels, every
     output bit for bit equal to the oracle's (plain, FP8 with and without the bf16 output,
-    MXFP4)."""
+    MXFP4). FARN_MANY_SHAPES=N runs N such calls instead of 18 (same seeds for the first 18),
+    printing one line per call."""
     rng = np.random.default_rng(2025)
-    for i in range(18):
+    n_calls = int(os.environ.get("FARN_MANY_SHAPES", "18"))
+    for i in range(n_calls):
         R = int(rng.integers(1, 9))
         T = int(np.exp(rng.uniform(np.log(300), np.log(4000))))
         H = int(rng.integers(1, 65)) * 128 if i % 6 else int(rng.integers(129, 257)) * 128
@@ -850,6 +852,9 @@ def test_random_shapes_many_rows_bit_exact(dev):
         assert np.array_equal(from_dev_bf16(ro), ref[0]), (i, "MXFP4 residual_out")
         assert out is None or np.array_equal(from_dev_bf16(out), ref[1]), (i, "MXFP4 out")
         assert np.array_equal(q.cpu().numpy(), ref[2]) and np.array_equal(sc.cpu().numpy(), ref[3]), (i, "MXFP4 codes")
+        if n_calls > 18:
+            print(f"many{i}: R={R} T={T} H={H} {variant} residual={u.res is not None} emit={emit}: bit-exact",
+                  flush=True)
         del u, d
 
 
