@@ -14,8 +14,9 @@
 //   lane-strided: lane l holds vectors l, l+L, l+2L, ... So every load instruction of a
 //   wave is 64 lanes x 16 B = 1 KiB contiguous, and a 128-channel quant group is
 //   exactly 16 consecutive lanes (one DPP row) of one vector slot.
-//   Per lane: the source issues the loads of the row's slots before consuming any (the
-//   compiler may still sink some below the first slot's fold); the partials are summed
+//   Per lane: with one or two slots the source issues the loads of all of them before
+//   consuming any (the compiler may still sink some below the first slot's fold; rows
+//   beyond 16384 channels, four slots, load one slot at a time); the partials are summed
 //   in fp32 in rank order, the residual added last, the sum rounded to bf16
 //   (residual_out) and kept packed in registers. The sum of squares
 //   (fp64) goes lane -> 16-lane DPP butterfly -> 4 rows via readlane -> one double
