@@ -523,6 +523,49 @@ def test_gamma_and_rstd_extremes(dev, eps):
         _same_codes(mq.cpu().numpy(), ref_m[2], msc.cpu().numpy(), ref_m[3], lambda c: np.zeros(c.shape, bool))
 
 
+# Rows whose rstd lies within 1.2e-9 (relative) above the bf16 midpoint 1 + 2^-8: the pattern
+# y = [1, c x 7] (c = 0.9375) repeated along H, gamma = 1, eps the binary32 value 0x3DC917E0, so
+# the mean of squares is the same at every H; the exact result of each 1 is 1 + 2^-7 (0x3F81),
+# and an rstd rounded to binary32 gives 1 (0x3F80). The same row pins the oracle.
+NEAR_MID_EPS = float(np.array([0x3DC917E0], np.uint32).view(np.float32)[0])
+
+
+@pytest.mark.parametrize("R,T,H", [(1, 3, 8), (8, 40, 128), (2, 70, 7168), (8, 9, 20480)])
+def test_rstd_near_bf16_midpoint(dev, R, T, H):
+    """The fp32 normalisation fast path must hand an element whose product lies this close to a
+    bf16 midpoint over to fp64, and the row's rstd must resolve it: every output equals the
+    oracle's bit for bit (plain, FP8 and MXFP4 where H allows), in both launch shapes."""
+    y = np.tile(np.array([0x3F80] + [0x3F70] * 7, np.uint16), (T, H // 8))
+    P = np.zeros((R, T, H), np.uint16)
+    P[0] = y
+    g = np.full(H, 0x3F80, np.uint16)
+    eps = NEAR_MID_EPS
+    ref_p = oracle.reduce_add_rmsnorm(P, None, g, eps, nthreads=ORACLE_THREADS)
+    assert (ref_p[1][:, 0::8] == 0x3F81).all()
+    ref_q = oracle.reduce_add_rmsnorm_quant_group(P, None, g, eps, 128, True, nthreads=ORACLE_THREADS) \
+        if H % 128 == 0 else None
+    ref_m = oracle.reduce_add_rmsnorm_mxfp4(P, None, g, eps, nthreads=ORACLE_THREADS) if H % 32 == 0 else None
+    Pd = [to_dev_bf16(P[r], dev) for r in range(R)]
+    gd = to_dev_bf16(g, dev)
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
+        say(f"[gpu] rstd near a bf16 midpoint R={R} T={T} H={H} variant={variant}")
+        ro, out = F.reduce_add_rmsnorm(Pd, None, gd, eps, variant=variant)
+        torch.cuda.synchronize()
+        for name, got, want in (("residual_out", ro, ref_p[0]), ("out", out, ref_p[1])):
+            rep = compare_bf16(name, from_dev_bf16(got), want)
+            assert rep["n_bit_diff"] == 0, rep
+        if ref_q is not None:
+            qro, qout, q, sc = F.reduce_add_rmsnorm_quant_group(Pd, None, gd, eps, variant=variant)
+            torch.cuda.synchronize()
+            assert compare_bf16("FP8 out", from_dev_bf16(qout), ref_q[1])["n_bit_diff"] == 0
+            assert np.array_equal(q.cpu().numpy(), ref_q[2]) and np.array_equal(sc.cpu().numpy(), ref_q[3])
+        if ref_m is not None:
+            mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(Pd, None, gd, eps, variant=variant)
+            torch.cuda.synchronize()
+            assert compare_bf16("MXFP4 out", from_dev_bf16(mout), ref_m[1])["n_bit_diff"] == 0
+            assert np.array_equal(mq.cpu().numpy(), ref_m[2]) and np.array_equal(msc.cpu().numpy(), ref_m[3])
+
+
 def test_graph_capture_replays_match_eager(dev):
     """The calls allocate nothing and never synchronise, so a serving loop can capture them in a
     HIP graph. Replay several times with the program's own eager work and synchronisations

@@ -235,6 +235,39 @@ def check_norm_vs_exact():
             assert list(out[t]) == want, (R, T, H, t)
 
 
+# A row chosen so that its rstd lies within 1.2e-9 (relative) of a bf16 midpoint: R = 1, H = 8,
+# y = [1, c, ..., c] with c = 0.9375, gamma = 1, eps the binary32 value 0x3DC917E0. Then
+# out[0] = bf16(rstd), and rstd sits just above M = 1 + 2^-8, the midpoint between 1 and
+# 1 + 2^-7. (c and eps came from a search over bf16 c and binary32 eps for rows where
+# binary32 statistics round out[0] the other way; the pin checks both facts below.)
+NEAR_MID_C = 0x3F70
+NEAR_MID_EPS_BITS = 0x3DC917E0
+
+
+def _near_mid_row():
+    eps = float(np.array([NEAR_MID_EPS_BITS], np.uint32).view(np.float32)[0])
+    y = np.array([[0x3F80] + [NEAR_MID_C] * 7], np.uint16)
+    return y[None], np.full(8, 0x3F80, np.uint16), eps
+
+
+def check_rstd_near_bf16_midpoint():
+    """out rounds y*rstd*gamma once with rstd resolved beyond binary32: on the row above, the
+    exact mean of squares m = ss/H + eps satisfies m * M^2 < 1 (rationals), so rstd > M and
+    out[0] is 1 + 2^-7 (0x3F81); rstd computed in binary32 gives 1 (0x3F80) there. The whole
+    row equals the exactly rounded one (60-digit rstd)."""
+    partials, gamma, eps = _near_mid_row()
+    c = bf16_bits_to_fraction(NEAR_MID_C)
+    m = (1 + 7 * c * c) / 8 + Fraction(eps)
+    M = 1 + Fraction(1, 256)
+    assert m * M * M < 1 and 1 - m * M * M < Fraction(1, 10 ** 8)
+    r32 = np.float32(1) / np.sqrt(np.float32(float((1 + 7 * c * c) / 8)) + np.float32(eps), dtype=np.float32)
+    assert Fraction(float(r32)) <= M  # binary32 statistics land on the other side of M
+    ro, out = oracle.reduce_add_rmsnorm(partials, None, gamma, eps)
+    assert list(ro[0]) == list(partials[0, 0])
+    assert out[0, 0] == 0x3F81, hex(out[0, 0])
+    assert list(out[0]) == exact_out_row(list(ro[0]), list(gamma), eps)
+
+
 def check_constant_rows():
     """A constant row y = c gives out = bf16(c/sqrt(c^2 + eps) * gamma): eps is added to the mean
     inside the square root. For |c| >> 1e-3 that is gamma * sign(c) bit for bit."""
@@ -514,6 +547,15 @@ def check_mxfp4_blocks():
                 step = 0.5 if abs(r) < 2 else (1.0 if abs(r) < 4 else 2.0)
                 err = abs(_decode_e2m1(codes[i]) - r)
                 assert err <= step / 2 or (abs(r) > 6 and codes[i] & 0x7 == 7), (t, b, i, r, codes[i])
+    # a block maximum of 2^-126: floor(log2 amax) - 2 = -128 is clamped to -127 (byte 0x00),
+    # so the codes are V / 2^-127: 2^-126 -> 2 (code 4), 3*2^-128 -> 1.5 (code 3), -2^-128 ->
+    # -0.5 (code 0x9); without the clamp the byte would wrap to 0xFF, the NaN scale
+    z = np.zeros((1, 32), np.uint16)
+    z[0, 0] = 0x0080  # 2^-126, the smallest normal bf16
+    z[0, 1] = 0x0060  # 3 * 2^-128 = 96 * 2^-133 (subnormal)
+    z[0, 2] = 0x8020  # -2^-128 = -32 * 2^-133
+    qz, sz = oracle.mxfp4(z)
+    assert sz[0, 0] == 0x00 and qz[0, 0] == 0x34 and qz[0, 1] == 0x09 and not qz[0, 2:].any(), (sz, qz)
     # nibble order: a block whose element 0 is the maximum and element 1 zero
     y = np.zeros((1, 32), np.float32)
     y[0, 0] = 4.0
@@ -573,7 +615,7 @@ ALL_CHECKS = [
     check_e4m3_encoder_exhaustive_bf16, check_e4m3_encoder_exact_near_ties, check_e4m3_golden_codes,
     check_worked_example_plain, check_worked_example_quant,
     check_integer_sums_exact, check_fold_order_and_precision, check_identities, check_reduce_vs_exact_sum,
-    check_norm_vs_exact, check_constant_rows, check_vs_torch_rms_norm, check_constant_gamma_rms,
+    check_norm_vs_exact, check_rstd_near_bf16_midpoint, check_constant_rows, check_vs_torch_rms_norm, check_constant_gamma_rms,
     check_scale_invariance,
     check_quant_scale_and_max_code, check_quant_codes_exact_small, check_quant_fp32_quotient_ties,
     check_quant_dequant_bound,
@@ -679,6 +721,26 @@ MUTANTS = [
      "for (int64_t t = j->tid + 1; t < j->T; t += j->nthreads)"),
     ("thread_last_not_started", "for (int k = 1; k < n; ++k) {\n        if (pthread_create",
      "for (int k = 1; k < n - 1; ++k) {\n        if (pthread_create"),
+    # signs, special codes and the ends of each format's range
+    ("bf16_sign_dropped", "const uint16_t sign = signbit(x) ? 0x8000u : 0u;", "const uint16_t sign = 0u;"),
+    ("e4m3_sign_dropped", "const uint8_t sign = signbit(x) ? 0x80u : 0u;", "const uint8_t sign = 0u;"),
+    ("e2m1_sign_dropped", "const uint8_t sign = signbit(x) ? 0x8u : 0u;", "const uint8_t sign = 0u;"),
+    ("e4m3_nan_as_max", "if (isnan(x)) return (uint8_t)(sign | 0x7Fu);", "if (isnan(x)) return (uint8_t)(sign | 0x7Eu);"),
+    ("e4m3_no_saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);", "if (a >= 1e30) return (uint8_t)(sign | 0x7Eu);"),
+    ("bf16_subnormal_quantum", "if (ex < -126) ex = -126;", "if (ex < -130) ex = -130;"),
+    ("e2m1_quantum_1_above_4", "(a < 4.0 ? 1.0 : 2.0)", "(a < 4.0 ? 1.0 : 1.0)"),
+    ("mx_scale_bias_126", "scales[t * B + b] = (uint8_t)(s + 127);", "scales[t * B + b] = (uint8_t)(s + 126);"),
+    ("mx_scale_clamp_dropped", "if (s < -127) s = -127;", ""),
+    # statistics in binary32 instead of binary64
+    ("ss_in_float", "    double ss = 0.0;\n    for (int64_t h = 0; h < H; ++h) {\n        double y",
+     "    float ss = 0.0f;\n    for (int64_t h = 0; h < H; ++h) {\n        float y"),
+    ("rstd_in_float", "double rstd = 1.0 / sqrt(ss / (double)H + (double)j->eps);",
+     "double rstd = (double)(1.0f / sqrtf((float)(ss / (double)H) + j->eps));"),
+    # the quant taken of residual_out instead of the normalised out
+    ("quant_of_residual_out", "double v = fabs(bf16_to_double(o[h]));",
+     "double v = fabs(bf16_to_double(j->residual_out[base + h]));",
+     "oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale))",
+     "oracle_e4m3fn_from_double((double)(bf16_to_float(j->residual_out[base + h]) / scale))"),
 ]
 
 
