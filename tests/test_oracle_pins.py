@@ -335,14 +335,23 @@ def _quant_case(seed, R, T, H, outliers=True):
 
 def check_quant_scale_and_max_code():
     """scale = binary32(amax / 448) recomputed from the group's bf16 out with IEEE single division,
-    and every group with amax > 0 holds a code of magnitude 448 (0x7E)."""
-    for seed, R, T, H in [(0, 4, 16, 4096), (1, 2, 3, 256), (2, 8, 2, 1024)]:
-        d, (ro, out, q, sc) = _quant_case(seed, R, T, H)
-        o = np.abs(bf16_bits_to_float(out)).reshape(T, H // 128, 128)
-        amax = o.max(axis=2).astype(np.float32)
-        assert np.array_equal(sc, amax / np.float32(448.0))
+    amax as torch.amax takes it (a NaN in the group makes it NaN), and every group with amax > 0
+    holds a code of magnitude 448 (0x7E); a group holding a NaN out (here from one NaN gamma
+    channel) has a NaN scale and only NaN codes, the other groups are untouched."""
+    cases = [(0, 4, 16, 4096, None), (1, 2, 3, 256, None), (2, 8, 2, 1024, None), (3, 2, 2, 512, 130)]
+    for seed, R, T, H, nan_ch in cases:
+        d = make_inputs(CONFIGS["decode_fp8"], seed=seed, R=R, T=T, H=H)
+        if nan_ch is not None:
+            d["gamma"][nan_ch] = 0x7FC0
+        ro, out, q, sc = oracle.reduce_add_rmsnorm_quant_group(d["partials"], d["residual"], d["gamma"], EPS, 128)
+        o = torch.from_numpy(bf16_bits_to_float(out)).abs().reshape(T, H // 128, 128)
+        amax = o.amax(dim=2).numpy().astype(np.float32)
+        assert np.array_equal(sc, amax / np.float32(448.0), equal_nan=True)
         qq = q.reshape(T, H // 128, 128) & 0x7F
-        assert np.all((qq == 0x7E).any(axis=2) | (amax == 0))
+        nan_grp = np.isnan(amax)
+        assert nan_grp.sum() == (0 if nan_ch is None else T)
+        assert np.all((qq == 0x7F).all(axis=2)[nan_grp])
+        assert np.all(((qq == 0x7E).any(axis=2) | (amax == 0))[~nan_grp])
 
 
 def _fp32_quotient(bits, s) -> Fraction:
@@ -741,6 +750,11 @@ MUTANTS = [
      "double v = fabs(bf16_to_double(j->residual_out[base + h]));",
      "oracle_e4m3fn_from_double((double)(bf16_to_float(o[h]) / scale))",
      "oracle_e4m3fn_from_double((double)(bf16_to_float(j->residual_out[base + h]) / scale))"),
+    # NaN and inf: a NaN ignored by the group maximum, NaN rounded to inf, inf to NaN
+    ("fp8_amax_ignores_nan", "if (v > amax || isnan(v)) amax = v;\n                if (isnan(amax)) break;\n            }\n            /* amax/448",
+     "if (v > amax) amax = v;\n            }\n            /* amax/448"),
+    ("bf16_nan_as_inf", "if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);", "if (isnan(x)) return (uint16_t)(sign | 0x7F80u);"),
+    ("bf16_inf_as_nan", "if (isinf(x)) return (uint16_t)(sign | 0x7F80u);", "if (isinf(x)) return (uint16_t)(sign | 0x7FC0u);"),
 ]
 
 
