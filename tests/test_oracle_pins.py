@@ -484,6 +484,17 @@ def check_quant_alone():
                 continue
             v = _fp32_quotient(xb[t, h], s)
             assert q[t, h] == e4m3fn_nearest(v, negative_zero=(xb[t, h] == 0x8000)), (t, h)
+    # a NaN in one group: that group's scale is NaN (torch.amax takes NaN as the maximum) and
+    # all its codes are NaN codes; the row's other groups are unchanged
+    xn = xb.copy()
+    xn[1, 300] = 0x7FC0
+    qn, scn = oracle.quant_group(xn)
+    amax_n = torch.from_numpy(bf16_bits_to_float(xn)).abs().reshape(4, 4, 128).amax(dim=2).numpy()
+    assert np.array_equal(scn, amax_n.astype(np.float32) / np.float32(448.0), equal_nan=True)
+    assert np.isnan(scn[1, 2]) and np.all(qn[1, 256:384] & 0x7F == 0x7F)
+    keep = np.ones(512, bool)
+    keep[256:384] = False
+    assert np.array_equal(qn[1, keep], q[1, keep]) and np.array_equal(qn[[0, 2, 3]], q[[0, 2, 3]])
 
 
 # ============================================================================ MXFP4
@@ -755,6 +766,8 @@ MUTANTS = [
      "if (v > amax) amax = v;\n            }\n            /* amax/448"),
     ("bf16_nan_as_inf", "if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);", "if (isnan(x)) return (uint16_t)(sign | 0x7F80u);"),
     ("bf16_inf_as_nan", "if (isinf(x)) return (uint16_t)(sign | 0x7F80u);", "if (isinf(x)) return (uint16_t)(sign | 0x7FC0u);"),
+    ("quant_alone_amax_ignores_nan", "if (v > amax || isnan(v)) amax = v;\n                if (isnan(amax)) break;\n            }\n            float scale",
+     "if (v > amax) amax = v;\n            }\n            float scale"),
 ]
 
 
