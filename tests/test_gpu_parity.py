@@ -523,6 +523,37 @@ def test_gamma_and_rstd_extremes(dev, eps):
         _same_codes(mq.cpu().numpy(), ref_m[2], msc.cpu().numpy(), ref_m[3], lambda c: np.zeros(c.shape, bool))
 
 
+@pytest.mark.parametrize("eps", [1.0, 1e30, float(np.finfo(np.float32).max)])
+def test_large_eps_and_aliased_partials(dev, eps):
+    """Any finite eps >= 0 is accepted: with eps = 1, 1e30 and the largest binary32 value rstd
+    falls to 1e-15 .. 5e-20 (the outputs tiny, FP8 scales below 2^-64 at the largest), and the
+    partials are four pointers to two buffers (aliasing each other, as the calls allow). Every
+    output equals the oracle's bit for bit, plain, FP8 and MXFP4, in both launch shapes."""
+    d = make_inputs(CONFIGS["decode_fp8"], seed=91, R=2, T=33, H=4096)
+    P = np.stack([d["partials"][0], d["partials"][1], d["partials"][0], d["partials"][1]])
+    res, g = d["residual"], d["gamma"]
+    ref_p = oracle.reduce_add_rmsnorm(P, res, g, eps, nthreads=ORACLE_THREADS)
+    ref_q = oracle.reduce_add_rmsnorm_quant_group(P, res, g, eps, 128, True, nthreads=ORACLE_THREADS)
+    ref_m = oracle.reduce_add_rmsnorm_mxfp4(P, res, g, eps, nthreads=ORACLE_THREADS)
+    if eps > 1e38:
+        assert (ref_q[3] < 2.0 ** -64).all() and (ref_q[3] > 0).all()
+    p0, p1 = to_dev_bf16(d["partials"][0], dev), to_dev_bf16(d["partials"][1], dev)
+    Pd = [p0, p1, p0, p1]
+    rd, gd = to_dev_bf16(res, dev), to_dev_bf16(g, dev)
+    for variant in (F.VARIANT_WIDE, F.VARIANT_NARROW):
+        say(f"[gpu] eps={eps} aliased partials variant={variant}")
+        ro, out = F.reduce_add_rmsnorm(Pd, rd, gd, eps, variant=variant)
+        qro, qout, q, sc = F.reduce_add_rmsnorm_quant_group(Pd, rd, gd, eps, variant=variant)
+        mro, mout, mq, msc = F.reduce_add_rmsnorm_mxfp4(Pd, rd, gd, eps, variant=variant)
+        torch.cuda.synchronize()
+        for name, got, want in (("residual_out", ro, ref_p[0]), ("out", out, ref_p[1]),
+                                ("FP8 out", qout, ref_q[1]), ("MXFP4 out", mout, ref_m[1])):
+            rep = compare_bf16(name, from_dev_bf16(got), want)
+            assert rep["n_bit_diff"] == 0, rep
+        assert np.array_equal(q.cpu().numpy(), ref_q[2]) and np.array_equal(sc.cpu().numpy(), ref_q[3])
+        assert np.array_equal(mq.cpu().numpy(), ref_m[2]) and np.array_equal(msc.cpu().numpy(), ref_m[3])
+
+
 # Rows whose rstd lies within 1.2e-9 (relative) above the bf16 midpoint 1 + 2^-8: the pattern
 # y = [1, c x 7] (c = 0.9375) repeated along H, gamma = 1, eps the binary32 value 0x3DC917E0, so
 # the mean of squares is the same at every H; the exact result of each 1 is 1 + 2^-7 (0x3F81),
