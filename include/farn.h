@@ -30,7 +30,8 @@
  *   scale[t,g] = amax_g |out| / 448  (fp32, correctly rounded)
  *   q[t,h]     = e4m3fn_rne(fl32(out[t,h] / scale[t,g]))  (OCP E4M3, satfinite; 0 when
  *                scale == 0; the quotient as an IEEE single division gives it, then one
- *                rounding to E4M3; a -0 out gives the -0 code 0x80)
+ *                rounding to E4M3; a -0 out gives the -0 code 0x80; a group holding a NaN
+ *                out has a NaN scale and NaN codes, 0x7F or 0xFF)
  *
  * Layout: every [T,H] buffer is row-major and contiguous (row stride H
  * elements); bf16 values are passed as raw 16-bit patterns; q holds one E4M3
