@@ -385,3 +385,26 @@ def test_binding_refuses_host_tensors():
     for call in calls:
         with pytest.raises(ValueError, match="on the GPU"):
             call()
+
+
+def test_package_refuses_to_load_without_its_library(tmp_path):
+    """There is no fallback path: a copy of the package without libfarn.so raises on import."""
+    import shutil
+    pkg = os.path.dirname(F.__file__)
+    dst = tmp_path / "tp_all_reduce_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    proc = subprocess.run(["python", "-c", "import tp_all_reduce_amd"], cwd=tmp_path,
+                          capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert proc.returncode != 0
+    assert "ImportError" in proc.stderr and "no fallback" in proc.stderr, proc.stderr[-500:]
+
+
+def test_product_never_uses_the_oracle():
+    """The oracle is test infrastructure: nothing in the package (binding, host layer, kernels)
+    imports, links or names it."""
+    pkg = os.path.dirname(F.__file__)
+    for root, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(root, name)).read()
+                assert not re.search(r"oracle", text, re.I), name
