@@ -135,7 +135,8 @@ farn_status farn_reduce_add_rmsnorm_mxfp4(const void *const *partials, int R, co
 /* Launch shapes of the one kernel (one workgroup per token row; H/8 16-byte vectors per row):
  *   FARN_VARIANT_WIDE   (1, also named FARN_VARIANT_LATENCY): one vector per lane, H/8 lanes
  *                       rounded up to a multiple of 64 (up to 1024 lanes at H = 8192); beyond
- *                       H = 8192, 1024 lanes with two or four vectors each. The fewest
+ *                       H = 8192, two vectors per lane up to H = 16384 and four beyond, on H/16
+ *                       or H/32 lanes rounded up to a multiple of 64 (at most 1024). The fewest
  *                       instructions per lane.
  *   FARN_VARIANT_NARROW (2, also named FARN_VARIANT_BANDWIDTH): about half as many lanes with
  *                       two vectors each, for 1024 < H <= 8192 (the WIDE launch otherwise):

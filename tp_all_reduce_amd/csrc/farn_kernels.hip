@@ -27,8 +27,9 @@
 //   double per wave does.
 //
 // Two launch shapes of the same kernel (chosen by the host from R, T and H, as measured):
-//   wide   - the widest row mapping (L up to 1024, one vector per lane up to H = 8192): the
-//            fewest instructions per lane.
+//   wide   - the widest row mapping (L up to 1024, one vector per lane up to H = 8192; beyond,
+//            two or four per lane on as few lanes as cover the row): the fewest instructions
+//            per lane.
 //   narrow - L about NV/2, two vectors per lane: half the waves per row, twice the loads in
 //            flight per lane. On MI355X it is the faster one for H = 6152 .. 8192 (the FP8
 //            prefill call at H = 7168 by 3-4 %, decode by 5-9 %), at H = 4616 .. 5120 for
@@ -547,7 +548,7 @@ __device__ __forceinline__ u32x4 norm_store(u32x4 yb, u32x4 gam, double rstd, fl
 }
 
 // gamma of the vector slot at byte offset `off`. The four-slot kernels (rows beyond 16384
-// channels, 1024 lanes, so at most 128 VGPRs per lane) load it slot by slot when they
+// channels, launch bound 1024 lanes, so at most 128 VGPRs per lane) load it slot by slot when they
 // normalise instead of holding all four slots' gamma through the row: measured on MI355X, that
 // removes their register spills (28-44 bytes per lane) and makes them 3-10 % faster.
 __device__ __forceinline__ u32x4 gamma_slot(const Params &k, uint32_t off) {
