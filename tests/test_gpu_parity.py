@@ -685,7 +685,20 @@ def test_unfused_blocks_and_compositions(dev, name):
     assert ok, why
 
 
-@pytest.mark.parametrize("H", [128, 4096, 7168, 16384, 32768])
+@pytest.mark.parametrize("H", [128, 4096, 7168, 10240, 16384, 20480, 32768])
+def test_reduce_alone_shapes(dev, H):
+    """The all-reduce alone at every launch shape (one vector per lane; two or four per lane
+    above H = 8192 on as few lanes as cover the row: 640 lanes at H = 10240 and 20480, 1024 at
+    16384 and 32768), bit for bit against the oracle's block."""
+    d = make_inputs(CONFIGS["decode_ds"], seed=H, R=8, T=7, H=H)
+    u = Uploaded(d, dev)
+    say(f"[gpu] reduce alone H={H}")
+    ar = F.reduce(u.P)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bf16(ar), oracle.reduce(d["partials"]))
+
+
+@pytest.mark.parametrize("H", [128, 4096, 7168, 10240, 16384, 20480, 32768])
 def test_quant_alone_shapes(dev, H):
     rng = np.random.default_rng(H)
     x = rng.standard_normal((5, H)).astype(np.float32)
